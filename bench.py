@@ -1,0 +1,268 @@
+"""Benchmark: decode attention over a q8_0 KV cache on one MI355X.
+
+Default run (one JSON line on stdout):
+  * value: device-resident decode-attention K/V throughput (GB/s) on the
+    4096-row, 40/8-head, head_dim-128 workload.  One step = attention over 64
+    distinct layer caches of that shape (570 MB, more than the 256 MB
+    Infinity Cache, so the data comes from HBM), launched from a captured HIP
+    graph so host launch overhead stays out of the timed region.  Inputs are
+    resident in HBM before timing starts.
+  * roofline: the decode kernel's algorithmic bytes per launch (visible K+V
+    rows + q + out) over its average launch duration (HIP events on the
+    launch stream), against 8 TB/s.
+  * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+    sample of the same workload.
+  * pipeline: per-token time of the host-resident 64-layer stack at 16384
+    rows, ordered (depth 0) vs pipelined (depth 1, 128 MiB ring), with the
+    measured pinned host-to-device link peak.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention K/V GB/s (% of HBM/host-link peak); ms/token ordered vs pipelined"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n_rows, n_head_kv, head_dim, n_head_q, n_seq=1):
+    """Visible K+V rows (each read once per KV head) plus q and out."""
+    row = n_head_kv * head_dim // 32 * 34
+    return n_seq * (2 * n_rows * row + 2 * n_head_q * head_dim * 4)
+
+
+# ---------------------------------------------------------------- device-resident
+
+def device_resident(args, torch, kvd, inputs):
+    c = inputs.config(1)
+    L = args.layers
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(c.seed)
+    ks, vs, qs, outs = [], [], [], []
+    for layer in range(L):
+        r = c.layer_rng(layer)
+        ks.append(torch.from_numpy(inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)).to(dev))
+        vs.append(torch.from_numpy(inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)).to(dev))
+        qs.append(torch.from_numpy(inputs.random_q(r, 1, c.n_head_q, c.head_dim)).to(dev))
+        outs.append(torch.empty_like(qs[-1]))
+    del rng
+    stream = torch.cuda.Stream(device=dev)
+    ws = kvd.Workspace()
+    # eager warm-up (also allocates the workspace outside capture)
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            kvd.attend_decode(qs[l], outs[l], [[(ks[l], vs[l], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for l in range(L):
+            kvd.attend_decode(qs[l], outs[l], [[(ks[l], vs[l], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    ms_step = ms / args.steps
+    launches = args.steps * L
+    us_launch = ms * 1e3 / launches
+    per_launch = algorithmic_bytes(c.n_ctx, c.n_head_kv, c.head_dim, c.n_head_q)
+    gbs = per_launch / (us_launch * 1e-6) / 1e9
+    # the replayed graph recomputes every layer's output; check one against eager
+    ref = torch.empty_like(outs[0])
+    with torch.cuda.stream(stream):
+        kvd.attend_decode(qs[0], ref, [[(ks[0], vs[0], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    if not torch.equal(ref, outs[0]):
+        raise RuntimeError("graph replay output differs from the eager call")
+    curve = {}
+    if args.curve:
+        for n in (16384, 32768, 131072):
+            curve[str(n)] = device_curve_point(torch, kvd, inputs, n, stream, ws)
+    return {
+        "ms_per_step": ms_step, "value": gbs, "us_per_launch": us_launch, "bytes_per_launch": per_launch,
+        "layers_per_step": L, "curve": curve,
+        "ws": ws, "q": qs[0], "k": ks[0], "v": vs[0],
+    }
+
+
+def device_curve_point(torch, kvd, inputs, n, stream, ws):
+    """GB/s of one launch over n rows, 8 distinct layers cycled (>= 285 MB apart)."""
+    c = inputs.config(1)
+    dev = torch.device("cuda:0")
+    reps = max(2, min(16, int(2.5e9 // (2 * n * c.row_bytes))))
+    ks, vs = [], []
+    for i in range(reps):
+        r = np.random.default_rng([c.seed, 1000 + i, n])
+        ks.append(torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev))
+        vs.append(torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev))
+    q = torch.from_numpy(inputs.random_q(np.random.default_rng(n), 1, c.n_head_q, c.head_dim)).to(dev)
+    out = torch.empty_like(q)
+    with torch.cuda.stream(stream):
+        for i in range(reps):
+            kvd.attend_decode(q, out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(reps):
+            kvd.attend_decode(q, out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nrep = 5
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(nrep):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (nrep * reps)
+    b = algorithmic_bytes(n, c.n_head_kv, c.head_dim, c.n_head_q)
+    del ks, vs
+    torch.cuda.empty_cache()
+    return {"us_per_launch": round(us, 3), "GBps": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+# ---------------------------------------------------------------- host link + pipeline
+
+def link_peak(torch):
+    """Pinned host -> device copy bandwidth (GB/s) at several sizes; the peak is the plateau."""
+    dev = torch.device("cuda:0")
+    res = {}
+    s = torch.cuda.Stream(device=dev)
+    for mib in (1, 16, 64, 256, 1024):
+        n = mib << 20
+        h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        d = torch.empty(n, dtype=torch.uint8, device=dev)
+        times = []
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(s):
+                e0.record(s)
+                d.copy_(h, non_blocking=True)
+                e1.record(s)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        t = float(np.median(times[1:]))
+        res[str(mib)] = round(n / (t * 1e-3) / 1e9, 2)
+        del h, d
+    return res
+
+
+def pipeline(args, torch, kvd, inputs):
+    from decode_attention_offloaded_amd import stack
+    c = inputs.config(2)
+    res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1),
+                                  budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=2, log=log)
+    return res
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(target_s=15.0):
+    import oracle
+    from decode_attention_offloaded_amd import inputs
+    c = inputs.config(1)
+    cores = len(os.sched_getaffinity(0))
+    r = c.layer_rng(0)
+    k = inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)
+    v = inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)
+    q = inputs.random_q(r, 1, c.n_head_q, c.head_dim)
+    t0 = time.perf_counter()
+    oracle.attend(q, [[(k, v, 0)]], c.n_head_kv, c.head_dim, threads=cores)
+    one = time.perf_counter() - t0
+    reps = max(1, int(target_s / max(one, 1e-3)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.attend(q, [[(k, v, 0)]], c.n_head_kv, c.head_dim, threads=cores)
+    dt = time.perf_counter() - t0
+    b = algorithmic_bytes(c.n_ctx, c.n_head_kv, c.head_dim, c.n_head_q)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(b * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "%d calls of the 4096-row, 40/8-head, head_dim-128 layer (fp64 oracle, OpenMP over "
+                      "query heads), %.1f s; %s" % (reps, dt, cpu),
+            "ms_per_layer": round(dt / reps * 1e3, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--curve", type=int, default=1)
+    ap.add_argument("--pipeline", type=int, default=1)
+    ap.add_argument("--pipe-layers", type=int, default=64)
+    ap.add_argument("--pipe-tokens", type=int, default=8)
+    ap.add_argument("--cpu-baseline", type=int, default=1)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decode_attention_offloaded_amd import inputs, kvd
+    kvd.lib()
+    log("device:", torch.cuda.get_device_name(0), kvd.version())
+    d = device_resident(args, torch, kvd, inputs)
+    log("device-resident: %.1f GB/s, %.3f us/launch" % (d["value"], d["us_per_launch"]))
+    out = {
+        "metric": METRIC,
+        "value": round(d["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode attention, device-resident q8_0 KV: 1 sequence x 4096 rows, 40 query / "
+                               "8 KV heads, head_dim 128; one step = 64 distinct layer caches",
+                   "n_ctx": 4096, "n_head_q": 40, "n_head_kv": 8, "head_dim": 128,
+                   "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
+        "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<128,5>", "bytes_per_launch": d["bytes_per_launch"],
+                     "us_per_launch": round(d["us_per_launch"], 3)},
+        "device_curve": d["curve"],
+    }
+    if args.pipeline:
+        out["pipeline"] = pipeline(args, torch, kvd, inputs)
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,707 @@
+// Split-K flash-decode attention over a q8_0 grouped-query KV cache (gfx950).
+//
+// What is computed (see include/kvd.h): for every sequence and query head h,
+// softmax over the visible rows of scale * q.k, times V, with query head h
+// reading KV head floor(h / G) ("F5 -- Advanced KV Cache Techniques", M3 What
+// shipped: query heads grouped by the GQA ratio), over q8_0 rows laid out
+// token-major with every KV head in a row (same page, M2 What shipped:
+// [head_dim, n_head_kv, n_kv]).  The split results are merged with the
+// online-softmax rule (same page, M4 step 6 and W4: partial attention results
+// merged by their running maxima and sums).
+//
+// Shape of the work.  One workgroup = two waves = one (sequence, KV head,
+// row range) split.  Each wave walks 64-row sub-tiles of its split:
+//   1. the sub-tile's K and V chunks (34-byte q8_0 blocks, head g only) are
+//      fetched with coalesced buffer loads (8-byte units for head_dim 128,
+//      4-byte for 64) into registers one sub-tile ahead, then copied into the
+//      wave's own LDS tile in row order;
+//   2. scores: one lane per row; the row's K bytes are realigned from LDS
+//      (v_alignbyte), each signed code is converted with one SDWA convert and
+//      multiplied by the G query rows held in SGPRs (scalar loads), the block
+//      scale is applied once per 32 codes;
+//   3. online softmax in the exp2 domain: wave maxima by shuffles, rescale of
+//      the running sums only when a maximum grows, p = exp2(s - m) per lane;
+//   4. values: 16 dimensions per lane (head_dim/16 lanes per row); each V
+//      code is converted once and used for all G query heads; p * d is folded
+//      per (row, block) so the inner loop is one FMA per head per value.
+// The two waves' states merge in LDS; a split with siblings writes an
+// unnormalised partial (m, l, o) to the workspace, and the last workgroup of a
+// (sequence, KV head) -- found with one agent-scope counter -- merges the
+// partials in split order, so the result depends only on the split plan.
+// No MFMA: one query row per head is not a dense contraction.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <type_traits>
+
+#include "kvd_internal.h"
+#include "kvd_plan.h"
+
+namespace kvd {
+namespace {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+// Constant address space: loads through it are scalar (s_load) when uniform.
+typedef const float __attribute__((address_space(4)))* const_f32_ptr;
+
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+
+struct SegDesc {
+    const uint8_t* k;
+    const uint8_t* v;
+    int32_t stride;   // row stride in bytes
+    int32_t row_lo;   // first visible row
+    int32_t n_vis;    // visible rows
+    int32_t n_split;  // splits over this segment
+    int32_t n_rows;   // readable rows
+    int32_t pad;
+};
+
+struct SeqDesc {
+    SegDesc seg[2];
+    int32_t split_base;  // first split of this sequence, relative to the launch
+    int32_t n_split;     // splits of this sequence
+};
+
+struct LaunchArgs {
+    SeqDesc seq[kMaxSeqPerLaunch];
+    const float* q;       // this launch's first sequence
+    float* out;           // this launch's first sequence
+    float* pm;            // partial maxima [split][n_head_q] (absolute split index)
+    float* pl;            // partial sums
+    float* po;            // partial outputs [split][n_head_q][D]
+    uint32_t* counters;   // [seq][n_head_kv], this launch's first sequence
+    int32_t n_seq;
+    int32_t n_head_kv;
+    int32_t split_rows;
+    int32_t n_items;
+    int32_t split_off;    // absolute index of this launch's first split
+    float scale_log2e;
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcWord3);
+}
+
+// DPP lane moves (gfx9 encodings).
+constexpr int kDppQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
+                                                                 CTRL, ROW_MASK, 0xf, false));
+}
+
+// Reductions over the 64 lanes of a wave; the result is wave-uniform (read
+// from lane 63 after the row broadcasts).
+__device__ inline float wave_max(float x) {
+    x = fmaxf(x, dpp<kDppQuadXor1>(x));
+    x = fmaxf(x, dpp<kDppQuadXor2>(x));
+    x = fmaxf(x, dpp<kDppRowHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppRowMirror>(x));
+    x = fmaxf(x, dpp<kDppRowBcast15, 0xa>(x));
+    x = fmaxf(x, dpp<kDppRowBcast31, 0xc>(x));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+__device__ inline float wave_sum(float x) {
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    x += dpp<kDppRowMirror>(x);
+    x += dpp<kDppRowBcast15, 0xa>(x);
+    x += dpp<kDppRowBcast31, 0xc>(x);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
+// Order the wave's LDS writes before reads by other lanes of the same wave
+// (and the reverse).  LDS ops of one wave execute in order; this keeps the
+// compiler from moving them and waits for outstanding LDS traffic.
+__device__ inline void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ inline float half_lo(uint32_t w) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    return (float)h;
+}
+
+__device__ inline float half_hi(uint32_t w) {
+    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    return (float)h;
+}
+
+__device__ inline float4 ldq4(const_f32_ptr p) { return make_float4(p[0], p[1], p[2], p[3]); }
+
+__device__ inline float sbyte(uint32_t w, int e) { return (float)(int8_t)(w >> (8 * e)); }
+
+template <int D>
+struct Geo {
+    static constexpr int NB = D / 32;                // q8_0 blocks per head
+    static constexpr int CB = 34 * NB;               // bytes of one head of one row
+    static constexpr int CW = CB / 4;                // ... in dwords
+    static constexpr int E = (CB % 8 == 0) ? 8 : 4;  // load unit
+    static constexpr int U = CB / E;                 // units per chunk (17)
+    static constexpr int LPR = D / 16;               // value-phase lanes per row
+    static constexpr int RPP = 64 / LPR;             // value-phase rows per pass
+    static_assert(U == 17, "chunk must be 17 load units");
+    static_assert(CB % 4 == 0, "chunk must be whole dwords");
+};
+
+template <int D>
+struct TileRegs {
+    typedef typename std::conditional<Geo<D>::E == 8, u32x2, uint32_t>::type unit_t;
+    unit_t u[17];
+};
+
+// Buffer descriptor for head g of the 64-row sub-tile starting at row0 of one
+// tensor (K or V).  Its range ends with head g's chunk in the last readable
+// row, so loads past the segment return zeros instead of touching memory.
+template <int D>
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, const SegDesc& sg, int g, int row0) {
+    using G_ = Geo<D>;
+    const int64_t head_off = (int64_t)row0 * sg.stride + (int64_t)g * G_::CB;
+    const int64_t lim64 = (int64_t)(sg.n_rows - 1 - row0) * sg.stride + G_::CB;
+    const int32_t lim = (int32_t)(lim64 > 0x7fffffff ? 0x7fffffff : lim64);
+    return make_rsrc(base + head_off, lim);
+}
+
+// Load-unit layout of one 64-row sub-tile of one head (17 units per row):
+//   instruction i < 16: rows 4i .. 4i+3, lane -> (row 4i + lane/16, unit lane%16)
+//   instruction 16    : every row's last unit, lane -> (row lane, unit 16)
+// so per-lane offsets are affine in i (one VGPR each) and each of the first 16
+// instructions reads four contiguous 128-byte runs.
+struct TileOffsets {
+    int32_t g_main;   // global byte offset of (row lane/16, unit lane%16)
+    int32_t g_last;   // global byte offset of (row lane, unit 16)
+    int32_t l_main;   // LDS byte offset of the same units in [64][17] packed rows
+    int32_t l_last;
+};
+
+template <int D>
+__device__ inline TileOffsets tile_offsets(int lane, int32_t stride) {
+    constexpr int E = Geo<D>::E;
+    TileOffsets t;
+    t.g_main = (lane >> 4) * stride + (lane & 15) * E;
+    t.g_last = lane * stride + 16 * E;
+    t.l_main = (17 * (lane >> 4) + (lane & 15)) * E;
+    t.l_last = (17 * lane + 16) * E;
+    return t;
+}
+
+template <int D>
+__device__ inline void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t rs, const TileOffsets& o, int32_t stride) {
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+        const int32_t voff = (i < 16) ? o.g_main + 4 * i * stride : o.g_last;
+        if constexpr (Geo<D>::E == 8) r.u[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0);
+        else r.u[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
+    }
+}
+
+template <int D>
+__device__ inline void store_tile(const TileRegs<D>& r, uint8_t* t, const TileOffsets& o) {
+    using unit_t = typename TileRegs<D>::unit_t;
+    constexpr int E = Geo<D>::E;
+#pragma unroll
+    for (int i = 0; i < 17; ++i) {
+        const int32_t loff = (i < 16) ? o.l_main + 68 * i * E : o.l_last;
+        *(unit_t*)(t + loff) = r.u[i];
+    }
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
+    using G_ = Geo<D>;
+    constexpr int NB = G_::NB, CB = G_::CB, CW = G_::CW, LPR = G_::LPR, RPP = G_::RPP;
+    static_assert(NB % 2 == 0, "head_dim must be a multiple of 64");
+    constexpr int GP = (G + 3) / 4 * 4;  // p row padded to float4
+
+    __shared__ __attribute__((aligned(16))) uint8_t s_tile[kWaves][2][kSubRows * CB];
+    __shared__ __attribute__((aligned(16))) float s_p[kWaves][kSubRows][GP];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // Workgroups go round-robin over the 8 XCDs; give each XCD a contiguous
+    // run of items so that the KV heads of one row range share an L2.
+    const int nblk = gridDim.x;
+    const int item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    if (item >= A.n_items) return;
+    const int lsplit = item / A.n_head_kv;
+    const int g = item - lsplit * A.n_head_kv;
+    int s = 0;
+    while (s + 1 < A.n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
+    const SeqDesc& SQ = A.seq[s];
+    int sp = lsplit - SQ.split_base;
+    int sgi = 0;
+    if (sp >= SQ.seg[0].n_split) {
+        sp -= SQ.seg[0].n_split;
+        sgi = 1;
+    }
+    const SegDesc& SG = SQ.seg[sgi];
+    const int r_begin = SG.row_lo + sp * A.split_rows;
+    const int r_end = min(r_begin + A.split_rows, SG.row_lo + SG.n_vis);
+    const int n_sub = (r_end - r_begin + kSubRows - 1) / kSubRows;
+    const int n_head_q = A.n_head_kv * G;
+    const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D;
+
+    const TileOffsets toff = tile_offsets<D>(lane, SG.stride);
+
+    uint8_t* tk = s_tile[wave][0];
+    uint8_t* tv = s_tile[wave][1];
+    float(*pw)[GP] = s_p[wave];
+
+    float m[G], l[G], o[G][16];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) o[h][k] = 0.f;
+    }
+
+    // value-phase lane roles
+    const int vpart = lane % LPR;            // which 16 dims
+    const int vrs = lane / LPR;              // row slot within a pass
+    const int vb = vpart >> 1;               // block
+    const int vsb = 34 * vb + 2 + 16 * (vpart & 1);  // first code byte within the chunk
+    const int vdw = vsb >> 2;                // first dword to read
+    const int vsh = vsb & 3;                 // 0 or 2
+    const int vdw4 = min(vdw + 4, CW - 1);   // 5th dword (only used when vsh == 2)
+
+    TileRegs<D> regs;
+    int t = wave;
+    if (t < n_sub) {
+        load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, r_begin + t * kSubRows), toff, SG.stride);
+        store_tile<D>(regs, tk, toff);
+        load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, r_begin + t * kSubRows), toff, SG.stride);
+        store_tile<D>(regs, tv, toff);
+    }
+    for (; t < n_sub; t += kWaves) {
+        const int row0 = r_begin + t * kSubRows;
+        const int nv = min(kSubRows, r_end - row0);
+        const bool has_next = t + kWaves < n_sub;
+        // next K in flight during this sub-tile's scores
+        if (has_next) load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + kWaves * kSubRows), toff, SG.stride);
+        wave_lds_sync();
+
+        // ---- scores, one lane per row
+        // The query is read with scalar loads, 4 dims x G heads at a time,
+        // one chunk ahead of its use.  Empty asm statements pin the order:
+        // the accumulators of chunk c-1 pass through one before the address
+        // of chunk c+1 is formed, so the loads are neither hoisted nor
+        // widened and the query never occupies more than two chunks of SGPRs.
+        float sc[G];
+        {
+            const uint32_t* rp = (const uint32_t*)(tk + lane * CB);
+            constexpr int NCH = D / 4;
+            float4 qc[G];
+            {
+                const_f32_ptr qp = (const_f32_ptr)qg;
+                asm volatile("" : "+s"(qp));
+#pragma unroll
+                for (int h = 0; h < G; ++h) qc[h] = ldq4(qp + h * D);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) sc[h] = 0.f;
+            uint32_t wn[9];
+#pragma unroll
+            for (int j = 0; j < 9; ++j) wn[j] = rp[j];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                // block b: scale at byte 34b, codes at bytes 34b+2 .. 34b+33
+                uint32_t w[9];
+#pragma unroll
+                for (int j = 0; j < 9; ++j) w[j] = wn[j];
+                if (b + 1 < NB) {
+                    const int nb0 = ((b + 1) % 2 == 0) ? 17 * (b + 1) / 2 : (17 * (b + 1) - 1) / 2;
+#pragma unroll
+                    for (int j = 0; j < 9; ++j) wn[j] = rp[nb0 + j];
+                }
+                float dot[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h) dot[h] = 0.f;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int c = 8 * b + kk;
+                    // chunk order: every head's accumulator passes through an
+                    // empty asm before the next chunk's address is formed
+#pragma unroll
+                    for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
+                    float4 qn[G];
+                    if (c + 1 < NCH) {
+                        const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
+                        asm volatile("" : "+s"(qp));
+#pragma unroll
+                        for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
+                    }
+                    const uint32_t x = (b % 2 == 0) ? __builtin_amdgcn_alignbyte(w[kk + 1], w[kk], 2) : w[kk + 1];
+                    const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        dot[h] = fmaf(qc[h].x, k0, dot[h]);
+                        dot[h] = fmaf(qc[h].y, k1, dot[h]);
+                        dot[h] = fmaf(qc[h].z, k2, dot[h]);
+                        dot[h] = fmaf(qc[h].w, k3, dot[h]);
+                    }
+                    if (c + 1 < NCH) {
+#pragma unroll
+                        for (int h = 0; h < G; ++h) qc[h] = qn[h];
+                    }
+                }
+                const float d = (b % 2 == 0) ? half_lo(w[0]) : half_hi(w[0]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) sc[h] = fmaf(d, dot[h], sc[h]);
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) sc[h] = (lane < nv) ? sc[h] * A.scale_log2e : -INFINITY;
+        }
+
+        // ---- online softmax (exp2 domain)
+        {
+            float mt[G];
+            bool grow = false;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                mt[h] = wave_max(sc[h]);
+                grow |= mt[h] > m[h];
+            }
+            if (grow) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mn = fmaxf(m[h], mt[h]);
+                    const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+                    l[h] *= alpha;
+#pragma unroll
+                    for (int k = 0; k < 16; ++k) o[h][k] *= alpha;
+                    m[h] = mn;
+                }
+            }
+            float pr[GP];
+#pragma unroll
+            for (int h = 0; h < GP; ++h) pr[h] = 0.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                pr[h] = __builtin_amdgcn_exp2f(sc[h] - m[h]);
+                l[h] += pr[h];
+            }
+#pragma unroll
+            for (int h = 0; h < GP; h += 4) *(float4*)&pw[lane][h] = make_float4(pr[h], pr[h + 1], pr[h + 2], pr[h + 3]);
+        }
+        wave_lds_sync();
+        if (has_next) {
+            store_tile<D>(regs, tk, toff);
+            // next V in flight during this sub-tile's values
+            load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, row0 + kWaves * kSubRows), toff, SG.stride);
+        }
+
+        // ---- values, 16 dims per lane, RPP rows per pass
+#pragma unroll 2
+        for (int pass = 0; pass < LPR; ++pass) {
+            const int r = pass * RPP + vrs;
+            const uint32_t* rowp = (const uint32_t*)(tv + r * CB);
+            uint32_t w0 = rowp[vdw], w1 = rowp[vdw + 1], w2 = rowp[vdw + 2], w3 = rowp[vdw + 3], w4 = rowp[vdw4];
+            uint32_t a0 = __builtin_amdgcn_alignbyte(w1, w0, vsh);
+            uint32_t a1 = __builtin_amdgcn_alignbyte(w2, w1, vsh);
+            uint32_t a2 = __builtin_amdgcn_alignbyte(w3, w2, vsh);
+            uint32_t a3 = __builtin_amdgcn_alignbyte(w4, w3, vsh);
+            const uint16_t dbits = *(const uint16_t*)(tv + r * CB + 34 * vb);
+            float d = (float)__builtin_bit_cast(_Float16, dbits);
+            d = (r < nv) ? d : 0.f;
+            float c[G];
+#pragma unroll
+            for (int h = 0; h < G; h += 4) {
+                const float4 pv = *(const float4*)&pw[r][h];
+                c[h] = pv.x * d;
+                if (h + 1 < G) c[h + 1] = pv.y * d;
+                if (h + 2 < G) c[h + 2] = pv.z * d;
+                if (h + 3 < G) c[h + 3] = pv.w * d;
+            }
+            const uint32_t aw[4] = {a0, a1, a2, a3};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float vv = sbyte(aw[kk], e);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) o[h][4 * kk + e] = fmaf(c[h], vv, o[h][4 * kk + e]);
+                }
+            }
+        }
+        wave_lds_sync();
+        if (has_next) store_tile<D>(regs, tv, toff);
+    }
+
+    // ---- wave state: total l; o summed over the row slots of each 16-lane
+    // row by DPP rotations, the four rows then go through LDS.
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] = wave_sum(l[h]);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            float x = o[h][k];
+            if constexpr (LPR == 4) x += dpp<kDppRowRor4>(x);
+            x += dpp<kDppRowRor8>(x);
+            o[h][k] = x;
+        }
+    }
+
+    // ---- merge the waves in LDS (reuses the tile memory)
+    __syncthreads();
+    float* mw = (float*)&s_tile[0][0][0];   // [kWaves][G]
+    float* lw = mw + kWaves * G;            // [kWaves][G]
+    float* ow = lw + kWaves * G;            // [kWaves][4 rows][G][D]
+    static_assert((2 * kWaves * G + kWaves * 4 * G * D) * 4 <= (int)sizeof(s_tile), "merge area");
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mw[wave * G + h] = m[h];
+            lw[wave * G + h] = l[h];
+        }
+    }
+    if ((lane & 15) < LPR) {
+        const int row16 = lane >> 4;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float* dst = ow + (((size_t)wave * 4 + row16) * G + h) * D + vpart * 16;
+#pragma unroll
+            for (int k = 0; k < 16; k += 4) *(float4*)(dst + k) = make_float4(o[h][k], o[h][k + 1], o[h][k + 2], o[h][k + 3]);
+        }
+    }
+    __syncthreads();
+
+    const int hq0 = g * G;  // first query head of this group
+    const bool single = SQ.n_split == 1;
+    const int abs_split = A.split_off + lsplit;
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, i = idx - (idx / D) * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, mw[w2 * G + h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+            const float mv = mw[w2 * G + h];
+            const float a = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+            L = fmaf(a, lw[w2 * G + h], L);
+            float ov = 0.f;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) ov += ow[(((size_t)w2 * 4 + r4) * G + h) * D + i];
+            O = fmaf(a, ov, O);
+        }
+        if (single) {
+            A.out[((size_t)s * n_head_q + hq0 + h) * D + i] = O / L;
+        } else {
+            const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
+            A.po[pi * D + i] = O;
+            if (i == 0) {
+                A.pm[pi] = M;
+                A.pl[pi] = L;
+            }
+        }
+    }
+    if (single) return;
+
+    // ---- last workgroup of this (sequence, KV head) merges the splits in order
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* ctr = A.counters + (size_t)s * A.n_head_kv + g;
+        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = prev == (uint32_t)(SQ.n_split - 1);
+        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    // Stage every split's (m, l) in LDS with one round of parallel loads,
+    // turn them into weights exp2(m - M) and the normaliser L per head, then
+    // sum the weighted partial outputs (S independent loads per output).
+    const int first = A.split_off + SQ.split_base;
+    const int S = SQ.n_split;  // <= kMaxSplits (the plan guarantees it)
+    float* sw = (float*)&s_tile[0][0][0];   // [G][S] maxima, then weights
+    float* sl = sw + G * kMaxSplits;        // [G][S] partial sums
+    float* sL = sl + G * kMaxSplits;        // [G] normalisers
+    static_assert((2 * G * kMaxSplits + G) * 4 <= (int)sizeof(s_tile), "combine area");
+    for (int idx = tid; idx < G * S; idx += kThreads) {
+        const int h = idx / S, k = idx - (idx / S) * S;
+        const size_t pi = (size_t)(first + k) * n_head_q + hq0 + h;
+        sw[h * kMaxSplits + k] = A.pm[pi];
+        sl[h * kMaxSplits + k] = A.pl[pi];
+    }
+    __syncthreads();
+    for (int h = wave; h < G; h += kWaves) {
+        float mx = -INFINITY;
+        for (int k = lane; k < S; k += 64) mx = fmaxf(mx, sw[h * kMaxSplits + k]);
+        mx = wave_max(mx);
+        float sum = 0.f;
+        for (int k = lane; k < S; k += 64) {
+            const float mv = sw[h * kMaxSplits + k];
+            const float w = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - mx);
+            sw[h * kMaxSplits + k] = w;
+            sum = fmaf(w, sl[h * kMaxSplits + k], sum);
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) sL[h] = sum;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, i = idx - (idx / D) * D;
+        const float* po = A.po + ((size_t)first * n_head_q + hq0 + h) * D + i;
+        const size_t step = (size_t)n_head_q * D;
+        const float* w = sw + h * kMaxSplits;
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+        int k = 0;
+        for (; k + 4 <= S; k += 4) {
+            o0 = fmaf(w[k], po[(size_t)k * step], o0);
+            o1 = fmaf(w[k + 1], po[(size_t)(k + 1) * step], o1);
+            o2 = fmaf(w[k + 2], po[(size_t)(k + 2) * step], o2);
+            o3 = fmaf(w[k + 3], po[(size_t)(k + 3) * step], o3);
+        }
+        for (; k < S; ++k) o0 = fmaf(w[k], po[(size_t)k * step], o0);
+        A.out[((size_t)s * n_head_q + hq0 + h) * D + i] = ((o0 + o1) + (o2 + o3)) / sL[h];
+    }
+}
+
+__global__ void zero_kernel(uint4* p, size_t n16, uint32_t* tail, size_t n4tail) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t j = i; j < n16; j += stride) p[j] = make_uint4(0, 0, 0, 0);
+    for (size_t j = i; j < n4tail; j += stride) tail[j] = 0;
+}
+
+typedef void (*kernel_fn)(const LaunchArgs);
+
+template <int D>
+kernel_fn pick_g(int G) {
+    switch (G) {
+        case 1: return decode_kernel<D, 1>;
+        case 2: return decode_kernel<D, 2>;
+        case 3: return decode_kernel<D, 3>;
+        case 4: return decode_kernel<D, 4>;
+        case 5: return decode_kernel<D, 5>;
+        case 6: return decode_kernel<D, 6>;
+        case 7: return decode_kernel<D, 7>;
+        case 8: return decode_kernel<D, 8>;
+    }
+    return nullptr;
+}
+
+kernel_fn pick_kernel(int D, int G) { return D == 128 ? pick_g<128>(G) : pick_g<64>(G); }
+
+}  // namespace
+}  // namespace kvd
+
+using namespace kvd;
+
+extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes) {
+    clear_error();
+    if (!bytes) return fail(KVD_EINVAL, "bytes is NULL");
+    AttendPlan p;
+    const int rc = plan_attend(args, &p);
+    if (rc != KVD_OK) return rc;
+    *bytes = p.ws_bytes;
+    return KVD_OK;
+}
+
+extern "C" int kvd_attend_workspace_init(void* workspace, size_t bytes, void* stream) {
+    clear_error();
+    if (bytes == 0) return KVD_OK;
+    if (!workspace || (uintptr_t)workspace % 16) return fail(KVD_EINVAL, "workspace must be non-NULL and 16-byte aligned");
+    const size_t n16 = bytes / 16;
+    const size_t n4 = (bytes - n16 * 16) / 4;
+    uint32_t* tail = (uint32_t*)((uint8_t*)workspace + n16 * 16);
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks < 1) blocks = 1;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)workspace, n16,
+                       tail, n4);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVD_EHIP, "workspace init launch: %s", hipGetErrorString(e));
+    return KVD_OK;
+}
+
+extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
+    clear_error();
+    AttendPlan p;
+    int rc = plan_attend(a, &p);
+    if (rc != KVD_OK) return rc;
+    if (p.ws_bytes > 0) {
+        if (!a->workspace || a->workspace_bytes < p.ws_bytes)
+            return fail(KVD_EINVAL, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
+                        a->workspace ? a->workspace_bytes : (size_t)0);
+        if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
+    }
+    const kernel_fn fn = pick_kernel(a->head_dim, p.group);
+    if (!fn) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
+
+    uint8_t* ws = (uint8_t*)a->workspace;
+    const int D = a->head_dim;
+    const int n_head_q = a->n_head_q;
+    const float scale_log2e = (float)((double)a->scale * 1.4426950408889634);
+
+    for (int s0 = 0; s0 < a->n_seq; s0 += kMaxSeqPerLaunch) {
+        const int ns = (a->n_seq - s0 < kMaxSeqPerLaunch) ? a->n_seq - s0 : kMaxSeqPerLaunch;
+        LaunchArgs L;
+        memset(&L, 0, sizeof(L));
+        const int64_t base0 = p.seq[s0].split_base;
+        int64_t nsplit = 0;
+        for (int j = 0; j < ns; ++j) {
+            const SeqPlan& sp = p.seq[s0 + j];
+            const kvd_kv_seg* segs = a->segs + (size_t)(s0 + j) * a->n_seg;
+            SeqDesc& d = L.seq[j];
+            for (int k = 0; k < 2; ++k) {
+                SegDesc& sd = d.seg[k];
+                const SegPlan& pl = sp.seg[k];
+                sd.n_split = pl.n_split;
+                sd.row_lo = pl.row_lo;
+                sd.n_vis = pl.n_vis;
+                sd.n_rows = pl.n_rows;
+                if (k < a->n_seg) {
+                    sd.k = (const uint8_t*)segs[k].k;
+                    sd.v = (const uint8_t*)segs[k].v;
+                    sd.stride = (int32_t)segs[k].row_stride;
+                }
+            }
+            d.split_base = (int32_t)(sp.split_base - base0);
+            d.n_split = sp.n_split;
+            nsplit += sp.n_split;
+        }
+        L.q = a->q + (size_t)s0 * n_head_q * D;
+        L.out = a->out + (size_t)s0 * n_head_q * D;
+        if (p.ws_bytes > 0) {
+            L.pm = (float*)(ws + p.off_pm);
+            L.pl = (float*)(ws + p.off_pl);
+            L.po = (float*)(ws + p.off_po);
+            L.counters = (uint32_t*)(ws + p.off_counters) + (size_t)s0 * a->n_head_kv;
+        }
+        L.n_seq = ns;
+        L.n_head_kv = a->n_head_kv;
+        L.split_rows = p.split_rows;
+        L.n_items = (int32_t)(nsplit * a->n_head_kv);
+        L.split_off = (int32_t)base0;
+        L.scale_log2e = scale_log2e;
+        const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);
+        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, L);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(KVD_EHIP, "decode kernel launch: %s", hipGetErrorString(e));
+    }
+    return KVD_OK;
+}

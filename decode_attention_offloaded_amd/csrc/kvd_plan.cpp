@@ -1,0 +1,152 @@
+// Split plan and argument validation for kvd_attend_decode (host only).
+#include "kvd_plan.h"
+
+#include <math.h>
+
+#include <algorithm>
+
+namespace kvd {
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
+    if (!a || !p) return fail(KVD_EINVAL, "null argument");
+    if (a->n_seq < 1 || a->n_seq > (1 << 20)) return fail(KVD_EINVAL, "n_seq %d out of range", a->n_seq);
+    if (a->n_head_kv < 1 || a->n_head_q < 1 || a->n_head_q % a->n_head_kv != 0)
+        return fail(KVD_EINVAL, "n_head_q %d must be a positive multiple of n_head_kv %d", a->n_head_q,
+                    a->n_head_kv);
+    const int G = a->n_head_q / a->n_head_kv;
+    if (G > 8) return fail(KVD_EINVAL, "GQA group %d > 8 is not supported", G);
+    if (a->n_head_kv > 4096) return fail(KVD_EINVAL, "n_head_kv %d out of range", a->n_head_kv);
+    if (a->head_dim != 64 && a->head_dim != 128)
+        return fail(KVD_EINVAL, "head_dim %d not supported (64 or 128)", a->head_dim);
+    if (a->n_seg != 1 && a->n_seg != 2) return fail(KVD_EINVAL, "n_seg %d must be 1 or 2", a->n_seg);
+    if (a->window < 0) return fail(KVD_EINVAL, "window %d < 0", a->window);
+    if (a->split_rows < 0 || a->split_rows % kSubRows != 0 || a->split_rows > (1 << 24))
+        return fail(KVD_EINVAL, "split_rows %d must be 0 or a positive multiple of 64", a->split_rows);
+    if (!isfinite(a->scale)) return fail(KVD_EINVAL, "scale is not finite");
+    if (!a->q || !a->out || !a->segs) return fail(KVD_EINVAL, "q, out and segs must not be NULL");
+    if ((uintptr_t)a->q % 4 || (uintptr_t)a->out % 4) return fail(KVD_EINVAL, "q/out must be 4-byte aligned");
+
+    const int D = a->head_dim;
+    const int chunk = D / 32 * 34;
+    const int64_t row_bytes = (int64_t)a->n_head_kv * chunk;
+    const int64_t align = (D == 128) ? 8 : 4;
+
+    p->group = G;
+    p->chunk_bytes = chunk;
+    p->seq.assign(a->n_seq, SeqPlan{});
+
+    int64_t total_sub = 0;
+    for (int s = 0; s < a->n_seq; ++s) {
+        const kvd_kv_seg* segs = a->segs + (size_t)s * a->n_seg;
+        for (int j = 0; j < a->n_seg; ++j) {
+            const kvd_kv_seg& g = segs[j];
+            if (g.n_rows < 0 || g.n_rows >= ((int64_t)1 << 31))
+                return fail(KVD_EINVAL, "seq %d seg %d: n_rows %lld out of range", s, j, (long long)g.n_rows);
+            if (g.pos0 < -((int64_t)1 << 62) || g.pos0 > ((int64_t)1 << 62))
+                return fail(KVD_EINVAL, "seq %d seg %d: pos0 out of range", s, j);
+            if (g.n_rows == 0) continue;
+            if (!g.k || !g.v) return fail(KVD_EINVAL, "seq %d seg %d: NULL k or v", s, j);
+            if (g.row_stride < row_bytes || g.row_stride >= ((int64_t)1 << 25))
+                return fail(KVD_EINVAL, "seq %d seg %d: row_stride %lld (row bytes %lld, limit 2^25)", s, j,
+                            (long long)g.row_stride, (long long)row_bytes);
+            if ((uintptr_t)g.k % align || (uintptr_t)g.v % align || g.row_stride % align)
+                return fail(KVD_EINVAL, "seq %d seg %d: k, v and row_stride must be %lld-byte aligned", s, j,
+                            (long long)align);
+        }
+        const kvd_kv_seg& last = segs[a->n_seg - 1];
+        int64_t qp;
+        if (a->q_pos) {
+            qp = a->q_pos[s];
+            if (qp < -((int64_t)1 << 62) || qp > ((int64_t)1 << 62))
+                return fail(KVD_EINVAL, "seq %d: q_pos out of range", s);
+        } else {
+            if (last.n_rows < 1) return fail(KVD_EINVAL, "seq %d: last segment is empty and q_pos is NULL", s);
+            qp = last.pos0 + last.n_rows - 1;
+        }
+        SeqPlan& sp = p->seq[s];
+        sp.q_pos = qp;
+        int64_t vis = 0;
+        for (int j = 0; j < 2; ++j) {
+            SegPlan& pl = sp.seg[j];
+            pl = SegPlan{0, 0, 0, 0};
+            if (j >= a->n_seg) continue;
+            const kvd_kv_seg& g = segs[j];
+            pl.n_rows = (int32_t)g.n_rows;
+            // visible: pos <= q_pos and (window == 0 or q_pos - pos < window)
+            int64_t lo = 0;
+            if (a->window > 0) lo = std::max<int64_t>(0, qp - a->window + 1 - g.pos0);
+            int64_t hi = std::min<int64_t>(g.n_rows, qp - g.pos0 + 1);
+            lo = std::min<int64_t>(lo, g.n_rows);
+            if (hi > lo) {
+                pl.row_lo = (int32_t)lo;
+                pl.n_vis = (int32_t)(hi - lo);
+            }
+            vis += pl.n_vis;
+            total_sub += ceil_div(pl.n_vis, kSubRows);
+        }
+        if (vis < 1) return fail(KVD_EINVAL, "seq %d: no row is visible to the query at position %lld", s,
+                                 (long long)qp);
+    }
+
+    // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
+    int64_t max_vis = 0;
+    for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
+    int64_t split_rows = a->split_rows;
+    if (split_rows == 0) {
+        const int64_t work = total_sub * a->n_head_kv;
+        const int64_t per_wave = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
+        split_rows = (int64_t)kSubRows * kWaves * per_wave;
+        // segments split separately: allow one extra split per segment
+        const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kSubRows) * kSubRows;
+        split_rows = std::max(split_rows, floor_rows);
+        if (split_rows > (1 << 24)) split_rows = 1 << 24;
+    }
+    p->split_rows = (int32_t)split_rows;
+
+    int64_t base = 0;
+    int32_t max_splits = 0;
+    for (int s = 0; s < a->n_seq; ++s) {
+        SeqPlan& sp = p->seq[s];
+        sp.split_base = base;
+        int32_t n = 0;
+        for (int j = 0; j < 2; ++j) {
+            sp.seg[j].n_split = (int32_t)ceil_div(sp.seg[j].n_vis, split_rows);
+            n += sp.seg[j].n_split;
+        }
+        sp.n_split = n;
+        max_splits = std::max(max_splits, n);
+        base += n;
+    }
+    p->total_splits = base;
+    p->max_splits = max_splits;
+    if (max_splits > kMaxSplits)
+        return fail(KVD_EINVAL, "split_rows %lld gives %d splits for one sequence (limit %d)", (long long)split_rows,
+                    max_splits, kMaxSplits);
+    if (base * a->n_head_kv >= ((int64_t)1 << 31) - 8) return fail(KVD_EINVAL, "too many work items");
+
+    if (max_splits <= 1) {
+        p->off_counters = p->off_pm = p->off_pl = p->off_po = 0;
+        p->ws_bytes = 0;
+    } else {
+        size_t off = 0;
+        p->off_counters = off;
+        off += round256((size_t)a->n_seq * a->n_head_kv * 4);
+        p->off_pm = off;
+        off += round256((size_t)base * a->n_head_q * 4);
+        p->off_pl = off;
+        off += round256((size_t)base * a->n_head_q * 4);
+        p->off_po = off;
+        off += round256((size_t)base * a->n_head_q * D * 4);
+        p->ws_bytes = off;
+    }
+    return KVD_OK;
+}
+
+}  // namespace kvd

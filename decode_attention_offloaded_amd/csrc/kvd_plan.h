@@ -1,0 +1,47 @@
+// Split plan for decode attention: visible row ranges, rows per split and the
+// workspace layout.  Host-only, HIP-free; depends on shapes and positions only.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "kvd_internal.h"
+
+namespace kvd {
+
+constexpr int kWaves = 2;               // waves per workgroup of the decode kernel
+constexpr int kSubRows = 64;            // rows per wave sub-tile (one row per lane)
+constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
+constexpr int64_t kTargetWaves = 2048;  // 256 CUs x 8 waves: enough sub-tiles to fill the chip
+constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
+
+struct SegPlan {
+    int32_t row_lo;   // first visible row (segment row index)
+    int32_t n_vis;    // visible rows
+    int32_t n_split;  // splits over this segment
+    int32_t n_rows;   // readable rows
+};
+
+struct SeqPlan {
+    SegPlan seg[2];
+    int32_t n_split;     // splits of the whole sequence
+    int64_t split_base;  // first global split index
+    int64_t q_pos;
+};
+
+struct AttendPlan {
+    int32_t group;        // G = n_head_q / n_head_kv
+    int32_t chunk_bytes;  // bytes of one head of one row: head_dim / 32 * 34
+    int32_t split_rows;
+    int32_t max_splits;   // largest per-sequence split count
+    int64_t total_splits;
+    std::vector<SeqPlan> seq;
+    size_t off_counters, off_pm, off_pl, off_po, ws_bytes;
+};
+
+// Validate every argument that does not need the GPU and build the plan.
+// Returns KVD_OK or KVD_EINVAL (with kvd_last_error text).
+int plan_attend(const kvd_attn_args* a, AttendPlan* p);
+
+}  // namespace kvd

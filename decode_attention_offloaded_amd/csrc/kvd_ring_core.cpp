@@ -1,0 +1,316 @@
+// Staging ring core (HIP-free).  See kvd_ring_core.h for the passages followed.
+#include "kvd_ring_core.h"
+
+#include <limits.h>
+
+#include <new>
+
+namespace kvd {
+
+bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t* need) {
+    if (depth <= 0) {
+        *need = 0;
+        return true;
+    }
+    const __int128 x = (__int128)(depth + 2) * 2 * (__int128)cap_rows * (__int128)row_bytes;
+    if (x < 0 || x > (__int128)INT64_MAX) return false;
+    *need = (int64_t)x;
+    return true;
+}
+
+Ring::Ring(std::unique_ptr<Transport> t, int32_t depth, int64_t budget)
+    : t_(std::move(t)), depth_(depth), budget_(budget), n_slots_(depth > 0 ? depth + 2 : 0) {
+    st_.depth = depth;
+    st_.n_slots = n_slots_;
+    st_.budget_bytes = budget;
+    st_.device = -1;
+}
+
+Ring::~Ring() { teardown(); }
+
+int Ring::validate(const kvd_stage_args* a) const {
+    if (!a) return fail(KVD_EINVAL, "args is NULL");
+    if (a->flags != KVD_STAGE_PREFETCH && a->flags != KVD_STAGE_ACQUIRE)
+        return fail(KVD_EINVAL, "flags %d must be KVD_STAGE_PREFETCH or KVD_STAGE_ACQUIRE", a->flags);
+    if (a->layer < 0) return fail(KVD_EINVAL, "layer %d < 0", a->layer);
+    if (!a->host_k || !a->host_v) return fail(KVD_EINVAL, "host_k/host_v must not be NULL");
+    if (a->row_bytes <= 0 || a->row_bytes % 4 != 0 || a->row_bytes > (1 << 24))
+        return fail(KVD_EINVAL, "row_bytes %lld must be a positive multiple of 4 (< 2^24)", (long long)a->row_bytes);
+    if (a->cap_rows < 1 || a->cap_rows >= ((int64_t)1 << 31))
+        return fail(KVD_EINVAL, "cap_rows %lld out of range", (long long)a->cap_rows);
+    if (a->n_rows < 1 || a->n_rows > a->cap_rows)
+        return fail(KVD_EINVAL, "n_rows %lld must be in [1, cap_rows %lld]", (long long)a->n_rows,
+                    (long long)a->cap_rows);
+    if (a->stable_rows < 0 || a->stable_rows > a->n_rows)
+        return fail(KVD_EINVAL, "stable_rows %lld must be in [0, n_rows %lld]", (long long)a->stable_rows,
+                    (long long)a->n_rows);
+    return KVD_OK;
+}
+
+bool Ring::busy() const {
+    for (const Slot& s : slots_)
+        if (s.state == STAGED || s.state == ACQUIRED) return true;
+    return false;
+}
+
+int Ring::find_layer(int32_t layer, int state) const {
+    for (size_t i = 0; i < slots_.size(); ++i)
+        if (slots_[i].state == state && slots_[i].layer == layer) return (int)i;
+    return -1;
+}
+
+int Ring::engage(int64_t slot_bytes) {
+    slots_.assign(n_slots_, Slot());
+    bool ok = t_->stream_create(&xfer_) == 0;
+    for (int i = 0; ok && i < n_slots_; ++i) {
+        Slot& s = slots_[i];
+        ok = t_->event_create(&s.ready) == 0 && t_->event_create(&s.rel) == 0 &&
+             t_->alloc((size_t)slot_bytes, &s.k) == 0 && t_->alloc((size_t)slot_bytes, &s.v) == 0;
+    }
+    if (!ok) {
+        // a failed allocation is a decline, not an error: undo everything
+        for (Slot& s : slots_) {
+            if (s.k) t_->release(s.k);
+            if (s.v) t_->release(s.v);
+            if (s.ready) t_->event_destroy(s.ready);
+            if (s.rel) t_->event_destroy(s.rel);
+        }
+        slots_.clear();
+        if (xfer_) t_->stream_destroy(xfer_);
+        xfer_ = nullptr;
+        return KVD_ENOMEM;
+    }
+    engaged_ = true;
+    slot_bytes_ = slot_bytes;
+    cursor_ = 0;
+    last_xfer_ = 0;
+    st_.ring_bytes = 2 * (int64_t)n_slots_ * slot_bytes;
+    return KVD_OK;
+}
+
+void Ring::teardown() {
+    if (!engaged_) return;
+    if (xfer_) t_->stream_sync(xfer_);
+    for (Slot& s : slots_)
+        if (s.released_once && s.rel) t_->event_sync(s.rel);
+    for (Slot& s : slots_) {
+        if (s.k) t_->release(s.k);
+        if (s.v) t_->release(s.v);
+        if (s.ready) t_->event_destroy(s.ready);
+        if (s.rel) t_->event_destroy(s.rel);
+    }
+    slots_.clear();
+    if (xfer_) t_->stream_destroy(xfer_);
+    xfer_ = nullptr;
+    engaged_ = false;
+    slot_bytes_ = 0;
+    cursor_ = 0;
+    last_xfer_ = 0;
+    st_.ring_bytes = 0;
+}
+
+int Ring::plan(const kvd_stage_args* a) {
+    if (depth_ == 0 || declined_) return KVD_DECLINED;
+    int64_t need;
+    if (!ring_need_bytes(depth_, a->cap_rows, a->row_bytes, &need)) need = INT64_MAX;
+    need_ = need;
+    st_.need_bytes = need;
+    int dev = -1;
+    if (t_->current_device(&dev) != 0) return fail(KVD_EHIP, "current device: %s", t_->error_text());
+    if (engaged_ && dev != device_)
+        return fail(KVD_ESTATE, "ring is bound to device %d but was called on device %d", device_, dev);
+    if (need > budget_) {
+        // checked before anything is allocated, on every plan; latched
+        if (engaged_) {
+            if (busy()) return fail(KVD_ESTATE, "ring would exceed its budget while deliveries are in flight");
+            teardown();
+        }
+        declined_ = true;
+        return KVD_DECLINED;
+    }
+    const int64_t slot_bytes = a->cap_rows * a->row_bytes;
+    if (engaged_ && slot_bytes > slot_bytes_) {
+        if (busy()) return fail(KVD_ESTATE, "slot capacity grew while deliveries are in flight");
+        teardown();
+    }
+    if (!engaged_) {
+        if (engage(slot_bytes) != KVD_OK) {
+            declined_ = true;
+            return KVD_DECLINED;
+        }
+        device_ = dev;
+        st_.device = dev;
+        st_.slot_rows = a->cap_rows;
+    }
+    return KVD_OK;
+}
+
+int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
+    const int s = (int)(cursor_ % (uint64_t)n_slots_);
+    Slot& S = slots_[s];
+    if (S.state == STAGED || S.state == ACQUIRED)
+        return fail(KVD_ESTATE,
+                    "slot %d still holds layer %d: release it before staging layer %d (look-ahead deeper than the ring)",
+                    s, S.layer, a->layer);
+    // stream to stream: the copy waits for the release of the slot's previous
+    // layer, recorded earlier in host order on the compute stream
+    if (S.released_once && t_->wait(xfer_, S.rel) != 0) return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
+    const size_t bytes = (size_t)rows * (size_t)a->row_bytes;
+    if (bytes > 0) {
+        if (t_->copy_h2d(S.k, a->host_k, bytes, xfer_) != 0 || t_->copy_h2d(S.v, a->host_v, bytes, xfer_) != 0)
+            return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
+    }
+    if (t_->record(S.ready, xfer_) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
+    S.state = STAGED;
+    S.layer = a->layer;
+    S.prefix_rows = rows;
+    S.row_bytes = a->row_bytes;
+    S.host_k = a->host_k;
+    S.host_v = a->host_v;
+    S.delivery = cursor_;
+    ++cursor_;
+    last_xfer_ = cursor_;
+    *slot_out = s;
+    return KVD_OK;
+}
+
+int Ring::ordered_acquire(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
+    if (!a->ordered_k || !a->ordered_v) return fail(KVD_EINVAL, "the ordered path needs ordered_k and ordered_v");
+    const size_t bytes = (size_t)a->n_rows * (size_t)a->row_bytes;
+    if (t_->copy_h2d(a->ordered_k, a->host_k, bytes, compute) != 0 ||
+        t_->copy_h2d(a->ordered_v, a->host_v, bytes, compute) != 0)
+        return fail(KVD_EHIP, "ordered copy: %s", t_->error_text());
+    st_.n_acquire_ordered++;
+    st_.bytes_ordered += 2 * (int64_t)bytes;
+    if (out) *out = kvd_slot_view{a->ordered_k, a->ordered_v, a->n_rows, a->row_bytes, 0, -1};
+    return KVD_DECLINED;
+}
+
+int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
+    int rc = validate(a);
+    if (rc != KVD_OK) return rc;
+    int pinned = 0;
+    const size_t span = (size_t)a->n_rows * (size_t)a->row_bytes;
+    if (t_->host_pinned(a->host_k, span, &pinned) != 0 || !pinned)
+        return fail(KVD_EINVAL, "host_k is not pinned host memory");
+    if (t_->host_pinned(a->host_v, span, &pinned) != 0 || !pinned)
+        return fail(KVD_EINVAL, "host_v is not pinned host memory");
+
+    if (a->flags == KVD_STAGE_PREFETCH) {
+        if (out) *out = kvd_slot_view{nullptr, nullptr, 0, 0, 0, -1};
+        rc = plan(a);
+        if (rc != KVD_OK) return rc;  // KVD_DECLINED: nothing to do
+        if (find_layer(a->layer, STAGED) >= 0 || find_layer(a->layer, ACQUIRED) >= 0)
+            return fail(KVD_ESTATE, "layer %d is already staged", a->layer);
+        int s = -1;
+        rc = deliver_prefix(a, a->stable_rows, &s);
+        if (rc != KVD_OK) return rc;
+        st_.n_prefetch++;
+        st_.bytes_early += 2 * a->stable_rows * a->row_bytes;
+        return KVD_OK;
+    }
+
+    // ACQUIRE
+    rc = plan(a);
+    if (rc == KVD_DECLINED) return ordered_acquire(a, compute, out);
+    if (rc != KVD_OK) return rc;
+    if (find_layer(a->layer, ACQUIRED) >= 0) return fail(KVD_ESTATE, "layer %d is already acquired", a->layer);
+    int s = find_layer(a->layer, STAGED);
+    if (s < 0) {
+        // not prefetched (e.g. the first layers of a step): stage the whole layer now
+        rc = deliver_prefix(a, a->n_rows, &s);
+        if (rc != KVD_OK) return rc;
+        st_.n_acquire_primed++;
+        st_.bytes_late += 2 * a->n_rows * a->row_bytes;
+    } else {
+        Slot& S = slots_[s];
+        if (S.row_bytes != a->row_bytes || S.host_k != a->host_k || S.host_v != a->host_v)
+            return fail(KVD_ESTATE, "ACQUIRE of layer %d does not match its PREFETCH (host buffers or row_bytes)",
+                        a->layer);
+        if (a->n_rows < S.prefix_rows)
+            return fail(KVD_ESTATE, "layer %d: n_rows %lld is below the prefetched prefix %lld", a->layer,
+                        (long long)a->n_rows, (long long)S.prefix_rows);
+        const int64_t tail = a->n_rows - S.prefix_rows;
+        if (tail > 0) {
+            const size_t off = (size_t)S.prefix_rows * (size_t)a->row_bytes;
+            const size_t n = (size_t)tail * (size_t)a->row_bytes;
+            void* dk = (uint8_t*)S.k + off;
+            void* dv = (uint8_t*)S.v + off;
+            const void* hk = (const uint8_t*)a->host_k + off;
+            const void* hv = (const uint8_t*)a->host_v + off;
+            if (last_xfer_ == S.delivery + 1) {
+                // this layer's prefix is the newest work on the transfer stream:
+                // the tail follows it there and `ready` moves behind the tail
+                if (t_->copy_h2d(dk, hk, n, xfer_) != 0 || t_->copy_h2d(dv, hv, n, xfer_) != 0 ||
+                    t_->record(S.ready, xfer_) != 0)
+                    return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
+            } else {
+                // later prefixes are queued on the transfer stream: do not wait
+                // behind them, copy the tail on the compute stream
+                if (t_->copy_h2d(dk, hk, n, compute) != 0 || t_->copy_h2d(dv, hv, n, compute) != 0)
+                    return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
+            }
+            st_.bytes_late += 2 * (int64_t)n;
+        }
+        st_.n_acquire_pipelined++;
+    }
+    Slot& S = slots_[s];
+    if (t_->wait(compute, S.ready) != 0) return fail(KVD_EHIP, "wait(ready): %s", t_->error_text());
+    S.state = ACQUIRED;
+    if (out) *out = kvd_slot_view{S.k, S.v, a->n_rows, a->row_bytes, 1, s};
+    return KVD_OK;
+}
+
+int Ring::release(int32_t layer, StreamH compute) {
+    if (!engaged_) return KVD_OK;  // ordered path: the copy lives on the compute stream
+    const int s = find_layer(layer, ACQUIRED);
+    if (s < 0) return fail(KVD_ESTATE, "layer %d is not acquired", layer);
+    Slot& S = slots_[s];
+    if (t_->record(S.rel, compute) != 0) return fail(KVD_EHIP, "record(release): %s", t_->error_text());
+    S.state = RELEASED;
+    S.released_once = true;
+    return KVD_OK;
+}
+
+void Ring::stats(kvd_ring_stats* out) const {
+    *out = st_;
+    out->engaged = engaged_ ? 1 : 0;
+    out->declined = declined_ ? 1 : 0;
+    out->device = engaged_ ? device_ : -1;
+    out->ring_bytes = engaged_ ? 2 * (int64_t)n_slots_ * slot_bytes_ : 0;
+}
+
+}  // namespace kvd
+
+using namespace kvd;
+
+extern "C" int kvd_ring_stage_layer(kvd_ring* ring, const kvd_stage_args* args, void* compute_stream,
+                                    kvd_slot_view* out) {
+    clear_error();
+    if (!ring) return fail(KVD_EINVAL, "ring is NULL");
+    try {
+        return ring->impl.stage(args, compute_stream, out);
+    } catch (const std::bad_alloc&) {
+        return fail(KVD_ENOMEM, "host allocation failed");
+    }
+}
+
+extern "C" int kvd_ring_release(kvd_ring* ring, int32_t layer, void* compute_stream) {
+    clear_error();
+    if (!ring) return fail(KVD_EINVAL, "ring is NULL");
+    return ring->impl.release(layer, compute_stream);
+}
+
+extern "C" int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, size_t out_size) {
+    clear_error();
+    if (!ring || !out) return fail(KVD_EINVAL, "ring and out must not be NULL");
+    if (out_size < sizeof(kvd_ring_stats))
+        return fail(KVD_EINVAL, "out_size %zu < sizeof(kvd_ring_stats) %zu", out_size, sizeof(kvd_ring_stats));
+    ring->impl.stats(out);
+    return KVD_OK;
+}
+
+extern "C" void kvd_ring_destroy(kvd_ring* ring) {
+    clear_error();
+    delete ring;
+}

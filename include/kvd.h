@@ -1,0 +1,255 @@
+/*
+ * kvd.h -- decode attention over a q8_0 grouped-query KV cache that may live in
+ * pinned host memory and reach the GPU one layer ahead (AMD Instinct MI355X,
+ * gfx950).
+ *
+ * Passages this interface follows (cited by page title and section):
+ *  [R4]  "sched: pipeline the delivery of a host-resident KV cache (R4)"
+ *        -- opening paragraph (deliver one split ahead on a transfer stream of
+ *        its own), What it does (1: stable prefix; 2: staging ring outside the
+ *        allocator with a ready/release event pair per slot; 3: two slots of
+ *        margin, deliveries issued after the consumer is enqueued, recycling
+ *        ordered stream to stream), the depth knob (0 = ordered path exactly),
+ *        Device memory (N + 2 slots of one layer's K+V; budget checked before
+ *        anything is allocated, latched, transport created lazily), What
+ *        tensor parallelism would take (an eligible backend needs async copies,
+ *        event record/wait and event creation; otherwise it declines rather
+ *        than racing; prefix delivery [0, prefix) and tail [prefix, nbytes)).
+ *  [F5]  "F5 -- Advanced KV Cache Techniques" -- M2 What shipped (KV view
+ *        [head_dim, n_head_kv, n_kv], innermost first), M3 What shipped (query
+ *        heads grouped by the GQA ratio), M4 step 6 and W4 (online-softmax merge
+ *        of partial attention results).
+ *  [LC]  "Plan: lossless long context -- derived hot/cold sizing (#5) +
+ *        host-RAM KV cold store (#3)" -- llama, sparse attention parity
+ *        boundary (model-native sliding-window attention).
+ *
+ * Conventions
+ *  - Every entry point validates all of its arguments before it enqueues
+ *    anything; on a negative return nothing was enqueued.
+ *  - Errors are returned as ints; kvd_last_error() gives text for the last
+ *    non-OK return on the calling thread.  No C++ exception crosses this ABI.
+ *  - "device pointer" = memory of the current HIP device (hipMalloc or torch);
+ *    "pinned host pointer" = hipHostMalloc / torch pin_memory memory.
+ *  - A stream argument is a hipStream_t passed as void* (NULL = null stream).
+ *  - The library never reads environment variables.
+ *
+ * Data layout (reading of [F5] M2; q8_0 itself is only named on the pages):
+ *  - q8_0 block: 34 bytes = little-endian binary16 scale d, then 32 int8
+ *    codes; value = d * code.
+ *  - A K (or V) row is one token: n_head_kv heads, each head_dim/32 blocks,
+ *    heads back to back (row bytes = n_head_kv * head_dim / 32 * 34; for
+ *    8 KV heads x 128 that is 1088).  Rows are row_stride bytes apart.
+ *    K and V are separate buffers with the same geometry.
+ *  - q and out: fp32 [n_seq][n_head_q][head_dim], contiguous.
+ *  - Query head h reads KV head floor(h / (n_head_q / n_head_kv)) ([F5] M3).
+ */
+#ifndef KVD_H
+#define KVD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ return codes */
+#define KVD_OK 0
+#define KVD_DECLINED 1      /* not an error: the ring is not engaged; the call
+                               used (or would use) the ordered path ([R4] depth
+                               knob and Device memory: declining falls back) */
+#define KVD_EINVAL (-1)     /* invalid argument; nothing enqueued */
+#define KVD_ENOMEM (-2)     /* host allocation failed */
+#define KVD_EHIP (-3)       /* a HIP runtime call failed (text in kvd_last_error) */
+#define KVD_ESTATE (-4)     /* call not valid in the object's current state
+                               (wrong device, out-of-order stage/release) */
+
+/* Text for the last non-OK return on this thread ("" if none).  The pointer
+ * stays valid until the next kvd_* call on the same thread. */
+const char* kvd_last_error(void);
+
+/* Library version string, e.g. "kvd 0.1.0 gfx950". */
+const char* kvd_version(void);
+
+/* ==================================================================== attention
+ * kvd_attend_decode: single-token decode attention over q8_0 K/V.
+ *
+ * For every sequence s and query head h (KV head g = floor(h/G)):
+ *   out[s,h,:] = sum_t softmax_t(scale * q[s,h,:] . K[t,g,:]) * V[t,g,:]
+ * over the rows t visible to the query ([R4] opening paragraph: the attention
+ * every decode token pays for).  A row at position p is visible to the query
+ * at position P iff p <= P and, when window > 0, P - p < window (reading of
+ * [LC]: the pages name sliding-window attention but give no formula).
+ *
+ * The rows of one sequence may come in one or two segments (e.g. an older
+ * part staged from host memory and a newer device-resident part); softmax is
+ * taken over the union of their visible rows ([F5] M4 step 6 / W4: partial
+ * results merged by the online-softmax rule).
+ *
+ * Work is split over (sequence, KV head, row range); each split keeps an
+ * online-softmax partial and the partials of one (sequence, KV head) are
+ * merged in a fixed order.  The split plan depends only on the shapes (never
+ * on pointers, timing or the ring), so two calls with equal shapes and equal
+ * input bytes give bit-identical outputs.
+ */
+typedef struct kvd_kv_seg {
+    const void* k;       /* device: K row 0 of this segment (q8_0 rows) */
+    const void* v;       /* device: V row 0 (same geometry as k) */
+    int64_t n_rows;      /* rows in the segment, 0 <= n_rows < 2^31; rows
+                            [0, n_rows) must be readable */
+    int64_t pos0;        /* token position of row 0 */
+    int64_t row_stride;  /* bytes between rows; >= row bytes; multiple of 8
+                            (head_dim 128) or 4 (head_dim 64); < 2^25 */
+} kvd_kv_seg;
+
+typedef struct kvd_attn_args {
+    int32_t n_seq;       /* >= 1 */
+    int32_t n_head_q;    /* multiple of n_head_kv; G = n_head_q/n_head_kv in 1..8 */
+    int32_t n_head_kv;   /* >= 1 */
+    int32_t head_dim;    /* 64 or 128 */
+    int32_t n_seg;       /* segments per sequence: 1 or 2 */
+    int32_t window;      /* 0 = full causal attention; W > 0 = sliding window */
+    int32_t split_rows;  /* 0 = plan from shape; else rows per split, a
+                            multiple of 64 (testing and tuning) */
+    float scale;         /* softmax scale, usually 1/sqrt(head_dim); finite */
+    const float* q;      /* device fp32 [n_seq][n_head_q][head_dim] */
+    float* out;          /* device fp32 [n_seq][n_head_q][head_dim] */
+    const kvd_kv_seg* segs;  /* HOST array [n_seq][n_seg]; read during the call only */
+    const int64_t* q_pos;    /* HOST array [n_seq] of query positions, or NULL =
+                                the position of the last row of the last segment */
+    void* workspace;         /* device scratch owned by the caller, or NULL if
+                                kvd_attend_workspace_bytes reports 0 */
+    size_t workspace_bytes;
+} kvd_attn_args;
+
+/* Bytes of workspace a call with these arguments needs (validates them too).
+ * Returns KVD_OK and sets *bytes, or KVD_EINVAL. */
+int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
+
+/* Zero-fill a workspace on `stream` with a small kernel (no memset node).
+ * A workspace must be zeroed once before its first use; every completed
+ * kvd_attend_decode leaves it zeroed again where that matters (split
+ * counters).  Calls that share a workspace must not overlap in time (use one
+ * stream, or order the streams). */
+int kvd_attend_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/* Enqueue decode attention on `stream` (asynchronous).  Returns KVD_OK,
+ * KVD_EINVAL (bad shapes, unaligned or null pointers, a sequence with no
+ * visible row, workspace too small) or KVD_EHIP (launch failure). */
+int kvd_attend_decode(const kvd_attn_args* args, void* stream);
+
+/* ==================================================================== staging ring
+ * A ring stages one attention layer's K and V from pinned host memory into
+ * device slots ahead of use ([R4] What it does 2 and 3).  It has depth N
+ * (look-ahead in layers) and N + 2 slots; each slot holds cap_rows rows of K
+ * and of V.  Its device cost is (N + 2) * 2 * cap_rows * row_bytes, checked
+ * against budget_bytes before anything is allocated, on every stage call;
+ * once over budget the ring declines for good ([R4] Device memory: checked
+ * before allocating, latched).  Slots, events and the transfer stream are
+ * created on the first stage call that engages the ring and freed by
+ * kvd_ring_destroy ([R4] Device memory: the transport is lazy).  Depth 0 is
+ * the ordered path exactly: it never allocates anything.
+ *
+ * Per layer l of a decode step the caller does:
+ *   1. write the newest row(s) of layer l into the pinned host K/V;
+ *   2. kvd_ring_stage_layer(flags = ACQUIRE, layer l) -> a view of l's K/V in
+ *      device memory, ordered on `compute` (the ordered path copies the whole
+ *      layer there; the pipelined path copies only the tail rows there and
+ *      waits for the prefix copied earlier on the transfer stream);
+ *   3. enqueue attention (kvd_attend_decode) on the view, on `compute`;
+ *   4. kvd_ring_release(layer l, compute): the slot is free once `compute`
+ *      passes this point;
+ *   5. kvd_ring_stage_layer(flags = PREFETCH, layer l + N): start copying the
+ *      stable prefix of layer l + N on the transfer stream.  It waits,
+ *      stream to stream, for the release of the slot it reuses ([R4] What it
+ *      does 3: issued after the consumer is enqueued, never a host sync).
+ * ACQUIRE of a layer that was not prefetched (e.g. the first N layers of a
+ * step) stages it on the spot.  A ring serves one host thread and one device.
+ */
+typedef struct kvd_ring kvd_ring;
+
+/* Create a ring.  depth >= 0 (0 = ordered path), budget in bytes (the pages'
+ * default is 128 MiB per device).  Does no device work.  Returns NULL iff
+ * depth < 0 or depth > 64 or host memory runs out (kvd_last_error says which). */
+kvd_ring* kvd_ring_create(int32_t depth, size_t budget_bytes);
+
+#define KVD_STAGE_PREFETCH 1
+#define KVD_STAGE_ACQUIRE 2
+
+typedef struct kvd_stage_args {
+    int32_t layer;        /* caller's layer id (>= 0); identifies the delivery */
+    int32_t flags;        /* KVD_STAGE_PREFETCH or KVD_STAGE_ACQUIRE */
+    const void* host_k;   /* PINNED host: K rows [cap_rows][row_bytes] of this layer */
+    const void* host_v;   /* PINNED host: V rows, same geometry */
+    int64_t row_bytes;    /* bytes of one K row (= one V row); multiple of 8 */
+    int64_t n_rows;       /* rows to deliver: [0, n_rows); 1 <= n_rows <= cap_rows */
+    int64_t stable_rows;  /* rows [0, stable_rows) are not written again before
+                             this layer's release ([R4] What it does 1: the stable
+                             prefix = the lowest row the step writes) */
+    int64_t cap_rows;     /* capacity the context may grow to; sizes the slots */
+    void* ordered_k;      /* device buffer >= n_rows*row_bytes, used when the ring
+                             is not engaged (ACQUIRE only; may be NULL for PREFETCH) */
+    void* ordered_v;
+} kvd_stage_args;
+
+typedef struct kvd_slot_view {
+    const void* k;        /* device: K rows [n_rows][row_bytes] */
+    const void* v;        /* device: V rows */
+    int64_t n_rows;
+    int64_t row_stride;   /* = row_bytes */
+    int32_t pipelined;    /* 1 = ring slot, 0 = ordered buffer */
+    int32_t slot;         /* slot index, or -1 */
+} kvd_slot_view;
+
+/* PREFETCH: returns KVD_OK (prefix copy enqueued on the transfer stream) or
+ *   KVD_DECLINED (ring not engaged: nothing done).  `out` may be NULL.
+ * ACQUIRE: returns KVD_OK with a slot view (pipelined) or KVD_DECLINED with a
+ *   view of ordered_k/ordered_v after enqueuing the whole-layer copy on
+ *   `compute`.  Either way the view is ready for work enqueued on `compute`
+ *   after this call and stays valid until kvd_ring_release(layer).
+ * Errors: KVD_EINVAL (null/pageable host pointers, bad row counts, missing
+ *   ordered buffers on the ordered path), KVD_ESTATE (a different device
+ *   than the ring's; reusing a slot whose previous layer was never released;
+ *   a layer staged twice; capacity changed while deliveries are in flight),
+ *   KVD_EHIP.  A failed device allocation is not an error: the ring declines
+ *   (latched) and ACQUIRE falls back to the ordered path. */
+int kvd_ring_stage_layer(kvd_ring* ring, const kvd_stage_args* args, void* compute_stream,
+                         kvd_slot_view* out);
+
+/* Mark the end of `layer`'s use of its slot: records the slot's release event
+ * on `compute` ([R4] What it does 2: the release half of the event pair).
+ * Call it after the last work that reads the view is enqueued.  No-op
+ * (KVD_OK) on the ordered path.  KVD_ESTATE if the layer is not acquired. */
+int kvd_ring_release(kvd_ring* ring, int32_t layer, void* compute_stream);
+
+typedef struct kvd_ring_stats {
+    int32_t depth;
+    int32_t n_slots;          /* depth + 2 when depth >= 1, else 0 */
+    int32_t engaged;          /* device resources currently allocated */
+    int32_t declined;         /* latched decline */
+    int32_t device;           /* HIP device the ring is bound to, or -1 */
+    int32_t reserved;
+    int64_t budget_bytes;
+    int64_t need_bytes;       /* size of the last plan: (N+2)*2*cap_rows*row_bytes */
+    int64_t ring_bytes;       /* device bytes held by slots now */
+    int64_t slot_rows;        /* rows per slot */
+    int64_t n_prefetch;       /* prefix deliveries issued ahead */
+    int64_t n_acquire_pipelined;  /* ACQUIREs served from a prefetched slot */
+    int64_t n_acquire_primed;     /* ACQUIREs that staged a slot on the spot */
+    int64_t n_acquire_ordered;    /* ACQUIREs on the ordered path */
+    int64_t bytes_early;      /* bytes copied by PREFETCH (ahead of use) */
+    int64_t bytes_late;       /* bytes copied at ACQUIRE into slots (tails, primes) */
+    int64_t bytes_ordered;    /* bytes copied on the ordered path */
+} kvd_ring_stats;
+
+/* Copy the counters into *out (out_size must be >= sizeof(kvd_ring_stats)). */
+int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, size_t out_size);
+
+/* Wait for the transfer stream and every slot's release, then free slots,
+ * events and the transfer stream.  NULL is a no-op. */
+void kvd_ring_destroy(kvd_ring* ring);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVD_H */

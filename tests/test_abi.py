@@ -1,0 +1,119 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point include/kvd.h declares, and rejects invalid arguments before it touches
+the GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from decode_attention_offloaded_amd import kvd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    with open(os.path.join(ROOT, "include", "kvd.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(kvd_\w+)\s*\(", text, flags=re.M):
+        names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kvd_attend_decode", "kvd_ring_create", "kvd_ring_stage_layer", "kvd_ring_release"} <= names
+    L = ctypes.CDLL(kvd.LIB_PATH)
+    missing = [n for n in sorted(names) if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_error_text():
+    assert kvd.version().startswith("kvd ")
+    assert isinstance(kvd.last_error(), str)
+
+
+def _args(**kw):
+    segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1088))
+    a = kvd.AttnArgs(1, 40, 8, 128, 1, 0, 0, 0.088, 0x1000, 0x2000, segs, None, None, 0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a, segs
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("head_dim", 256), ("n_head_q", 41), ("n_head_q", 72),
+                                         ("n_seg", 3), ("n_seq", 0), ("window", -1), ("split_rows", 100),
+                                         ("q", None), ("out", None)])
+def test_attend_rejects_bad_arguments(field, value):
+    a, keep = _args(**{field: value})
+    assert kvd.lib().kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    assert kvd.last_error()
+
+
+def test_attend_rejects_bad_segments():
+    L = kvd.lib()
+    for seg in [kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1000),      # stride below the row bytes
+                kvd.KvSeg(0x10004, 0x20000, 4096, 0, 1088),      # k not 8-byte aligned (head_dim 128)
+                kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1092),      # stride not 8-byte aligned
+                kvd.KvSeg(None, 0x20000, 4096, 0, 1088),         # NULL k
+                kvd.KvSeg(0x10000, 0x20000, -1, 0, 1088)]:       # negative rows
+        a, _ = _args()
+        segs = (kvd.KvSeg * 1)(seg)
+        a.segs = segs
+        assert L.kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL, seg.row_stride
+
+
+def test_attend_rejects_empty_visible_set():
+    a, _ = _args()
+    qp = (ctypes.c_int64 * 1)(-5)   # query before every row
+    a.q_pos = qp
+    assert kvd.lib().kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    a.q_pos = None
+    a.window = 0
+    segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 0, 0, 1088))   # no rows at all
+    a.segs = segs
+    assert kvd.lib().kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+
+
+def test_workspace_plan():
+    a, _ = _args()
+    n = kvd.workspace_bytes(a)
+    # 4096 rows x 8 KV heads = 512 sub-tiles of 64 rows: 128-row splits, 32 per head
+    splits = 32
+    expect = 256 + 2 * ((splits * 40 * 4 + 255) // 256 * 256) + splits * 40 * 128 * 4
+    assert n == expect
+    short, _ = _args()
+    short.segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 100, 0, 1088))
+    assert kvd.workspace_bytes(short) == 0   # a single split writes the output directly
+    forced, _ = _args(split_rows=4096)
+    assert kvd.workspace_bytes(forced) == 0
+
+
+def test_workspace_too_small_is_rejected():
+    a, _ = _args()
+    a.workspace = 0x100000
+    a.workspace_bytes = 1024
+    assert kvd.lib().kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+
+
+def test_ring_create_and_stats_without_device_work():
+    L = kvd.lib()
+    assert not L.kvd_ring_create(-1, 1 << 20)
+    assert not L.kvd_ring_create(65, 1 << 20)
+    r = kvd.Ring(1, 128 << 20)
+    st = r.stats()
+    assert (st["depth"], st["n_slots"], st["engaged"], st["declined"], st["ring_bytes"]) == (1, 3, 0, 0, 0)
+    small = kvd.RingStats()
+    assert L.kvd_ring_stats_get(r._h, ctypes.byref(small), 8) == kvd.KVD_EINVAL
+    # argument checks come before any HIP call
+    with pytest.raises(kvd.KvdError) as e:
+        r.stage(0, kvd.STAGE_ACQUIRE, 0x1000, 0x2000, 1088, 10, 9, 5, stream=0)  # n_rows > cap_rows
+    assert e.value.code == kvd.KVD_EINVAL
+    with pytest.raises(kvd.KvdError):
+        r.stage(0, 7, 0x1000, 0x2000, 1088, 10, 9, 10, stream=0)  # bad flags
+    with pytest.raises(kvd.KvdError):
+        r.stage(0, kvd.STAGE_PREFETCH, 0x1000, 0x2000, 1088, 10, 11, 10, stream=0)  # stable > n_rows
+    r.close()
+    L.kvd_ring_destroy(None)
