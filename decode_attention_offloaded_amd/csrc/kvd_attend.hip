@@ -9,8 +9,9 @@
 // online-softmax rule (same page, M4 step 6 and W4: partial attention results
 // merged by their running maxima and sums).
 //
-// Shape of the work.  One workgroup = two waves = one (sequence, KV head,
-// row range) split.  Each wave walks 64-row sub-tiles of its split:
+// Shape of the work.  One workgroup = NW waves (2, or 8 for long contexts) =
+// one (sequence, KV head, row range) split.  Each wave walks 64-row sub-tiles
+// of its split:
 //   1. the sub-tile's K and V chunks (34-byte q8_0 blocks, head g only) are
 //      fetched with coalesced buffer loads (8-byte units for head_dim 128,
 //      4-byte for 64) into registers one sub-tile ahead, then copied into the
@@ -24,10 +25,12 @@
 //   4. values: 16 dimensions per lane (head_dim/16 lanes per row); each V
 //      code is converted once and used for all G query heads; p * d is folded
 //      per (row, block) so the inner loop is one FMA per head per value.
-// The two waves' states merge in LDS; a split with siblings writes an
-// unnormalised partial (m, l, o) to the workspace, and the last workgroup of a
-// (sequence, KV head) -- found with one agent-scope counter -- merges the
-// partials in split order, so the result depends only on the split plan.
+// The waves' states merge in LDS; a split with siblings writes an
+// unnormalised partial (m, l, o) to the workspace and a second, small launch
+// merges the partials of each (sequence, KV head) in split order, so the
+// result depends only on the split plan.  (Merging inside the first launch
+// would need device-scope release/acquire between workgroups, which on this
+// chip writes back and invalidates the whole L2 of an XCD per workgroup.)
 // No MFMA: one query row per head is not a dense contraction.
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -46,7 +49,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Constant address space: loads through it are scalar (s_load) when uniform.
 typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
 struct SegDesc {
@@ -73,7 +75,6 @@ struct LaunchArgs {
     float* pm;            // partial maxima [split][n_head_q] (absolute split index)
     float* pl;            // partial sums
     float* po;            // partial outputs [split][n_head_q][D]
-    uint32_t* counters;   // [seq][n_head_kv], this launch's first sequence
     int32_t n_seq;
     int32_t n_head_kv;
     int32_t split_rows;
@@ -125,12 +126,14 @@ __device__ inline float wave_sum(float x) {
 }
 
 // Order the wave's LDS writes before reads by other lanes of the same wave
-// (and the reverse).  LDS ops of one wave execute in order; this keeps the
-// compiler from moving them and waits for outstanding LDS traffic.
+// (and the reverse).  The LDS executes one wave's instructions in issue order,
+// so only the compiler has to be kept from moving accesses across this point:
+// wavefront-scope fences do that without a wait.  (A workgroup-scope fence
+// would also wait for every outstanding global load -- the prefetched tile.)
 __device__ inline void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 __device__ inline float half_lo(uint32_t w) {
@@ -144,6 +147,21 @@ __device__ inline float half_hi(uint32_t w) {
 }
 
 __device__ inline float4 ldq4(const_f32_ptr p) { return make_float4(p[0], p[1], p[2], p[3]); }
+
+// Touch every 64-byte line of this group's query rows with scalar loads and
+// wait once (one round trip, overlapping the first tile's loads), so the
+// chunked scalar loads of the score phase hit the scalar cache.
+template <int N>
+__device__ inline void warm_query(const float* qg) {
+    constexpr int LINES = N / 16;
+    const_f32_ptr p = (const_f32_ptr)qg;
+    asm volatile("" : "+s"(p));
+    float t[LINES];
+#pragma unroll
+    for (int c = 0; c < LINES; ++c) t[c] = p[c * 16];
+#pragma unroll
+    for (int c = 0; c < LINES; ++c) asm volatile("" ::"s"(t[c]));
+}
 
 __device__ inline float sbyte(uint32_t w, int e) { return (float)(int8_t)(w >> (8 * e)); }
 
@@ -222,16 +240,16 @@ __device__ inline void store_tile(const TileRegs<D>& r, uint8_t* t, const TileOf
     }
 }
 
-template <int D, int G>
-__global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
+template <int D, int G, int NW>
+__global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
+    constexpr int kThreads = 64 * NW;
     using G_ = Geo<D>;
     constexpr int NB = G_::NB, CB = G_::CB, CW = G_::CW, LPR = G_::LPR, RPP = G_::RPP;
     static_assert(NB % 2 == 0, "head_dim must be a multiple of 64");
     constexpr int GP = (G + 3) / 4 * 4;  // p row padded to float4
 
-    __shared__ __attribute__((aligned(16))) uint8_t s_tile[kWaves][2][kSubRows * CB];
-    __shared__ __attribute__((aligned(16))) float s_p[kWaves][kSubRows][GP];
-    __shared__ int s_last;
+    __shared__ __attribute__((aligned(16))) uint8_t s_tile[NW][2][kSubRows * CB];
+    __shared__ __attribute__((aligned(16))) float s_p[NW][kSubRows][GP];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -287,17 +305,20 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
     TileRegs<D> regs;
     int t = wave;
     if (t < n_sub) {
+        // first sub-tile: K and V in flight together
+        TileRegs<D> regs_v;
         load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, r_begin + t * kSubRows), toff, SG.stride);
+        load_tile<D>(regs_v, tile_rsrc<D>(SG.v, SG, g, r_begin + t * kSubRows), toff, SG.stride);
+        warm_query<G * D>(qg);
         store_tile<D>(regs, tk, toff);
-        load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, r_begin + t * kSubRows), toff, SG.stride);
-        store_tile<D>(regs, tv, toff);
+        store_tile<D>(regs_v, tv, toff);
     }
-    for (; t < n_sub; t += kWaves) {
+    for (; t < n_sub; t += NW) {
         const int row0 = r_begin + t * kSubRows;
         const int nv = min(kSubRows, r_end - row0);
-        const bool has_next = t + kWaves < n_sub;
+        const bool has_next = t + NW < n_sub;
         // next K in flight during this sub-tile's scores
-        if (has_next) load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + kWaves * kSubRows), toff, SG.stride);
+        if (has_next) load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + NW * kSubRows), toff, SG.stride);
         wave_lds_sync();
 
         // ---- scores, one lane per row
@@ -407,7 +428,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
         if (has_next) {
             store_tile<D>(regs, tk, toff);
             // next V in flight during this sub-tile's values
-            load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, row0 + kWaves * kSubRows), toff, SG.stride);
+            load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, row0 + NW * kSubRows), toff, SG.stride);
         }
 
         // ---- values, 16 dims per lane, RPP rows per pass
@@ -463,10 +484,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
 
     // ---- merge the waves in LDS (reuses the tile memory)
     __syncthreads();
-    float* mw = (float*)&s_tile[0][0][0];   // [kWaves][G]
-    float* lw = mw + kWaves * G;            // [kWaves][G]
-    float* ow = lw + kWaves * G;            // [kWaves][4 rows][G][D]
-    static_assert((2 * kWaves * G + kWaves * 4 * G * D) * 4 <= (int)sizeof(s_tile), "merge area");
+    float* mw = (float*)&s_tile[0][0][0];   // [NW][G]
+    float* lw = mw + NW * G;            // [NW][G]
+    float* ow = lw + NW * G;            // [NW][4 rows][G][D]
+    static_assert((2 * NW * G + NW * 4 * G * D) * 4 <= (int)sizeof(s_tile), "merge area");
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -492,10 +513,10 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
         const int h = idx / D, i = idx - (idx / D) * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, mw[w2 * G + h]);
+        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, mw[w2 * G + h]);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) {
+        for (int w2 = 0; w2 < NW; ++w2) {
             const float mv = mw[w2 * G + h];
             const float a = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
             L = fmaf(a, lw[w2 * G + h], L);
@@ -515,96 +536,93 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const LaunchArgs A) {
             }
         }
     }
-    if (single) return;
+}
 
-    // ---- last workgroup of this (sequence, KV head) merges the splits in order
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        uint32_t* ctr = A.counters + (size_t)s * A.n_head_kv + g;
-        const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = prev == (uint32_t)(SQ.n_split - 1);
-        if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Stage every split's (m, l) in LDS with one round of parallel loads,
-    // turn them into weights exp2(m - M) and the normaliser L per head, then
-    // sum the weighted partial outputs (S independent loads per output).
+// Merge the split partials of one (sequence, query head) in split order: one
+// workgroup per (sequence, query head), one thread per dimension.  The split
+// maxima and sums go through LDS once; each thread then keeps 16 independent
+// loads of partial outputs in flight.  A separate launch, so the partials
+// written by the decode kernel are visible without cache maintenance inside a
+// kernel.
+template <int D>
+__global__ void __launch_bounds__(D) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
+    __shared__ float sw[kMaxSplits];  // maxima, then weights
+    __shared__ float sl[kMaxSplits];  // partial sums
+    __shared__ float sL;
+    const int i = threadIdx.x;
+    const int lane = i & 63;
+    const int hq = blockIdx.x % n_head_q;
+    const int s = blockIdx.x / n_head_q;
+    const SeqDesc& SQ = A.seq[s];
+    const int S = SQ.n_split;
+    if (S <= 1) return;  // written directly by the decode kernel
     const int first = A.split_off + SQ.split_base;
-    const int S = SQ.n_split;  // <= kMaxSplits (the plan guarantees it)
-    float* sw = (float*)&s_tile[0][0][0];   // [G][S] maxima, then weights
-    float* sl = sw + G * kMaxSplits;        // [G][S] partial sums
-    float* sL = sl + G * kMaxSplits;        // [G] normalisers
-    static_assert((2 * G * kMaxSplits + G) * 4 <= (int)sizeof(s_tile), "combine area");
-    for (int idx = tid; idx < G * S; idx += kThreads) {
-        const int h = idx / S, k = idx - (idx / S) * S;
-        const size_t pi = (size_t)(first + k) * n_head_q + hq0 + h;
-        sw[h * kMaxSplits + k] = A.pm[pi];
-        sl[h * kMaxSplits + k] = A.pl[pi];
+    for (int k = i; k < S; k += D) {
+        const size_t pi = (size_t)(first + k) * n_head_q + hq;
+        sw[k] = A.pm[pi];
+        sl[k] = A.pl[pi];
     }
     __syncthreads();
-    for (int h = wave; h < G; h += kWaves) {
+    if (i < 64) {
         float mx = -INFINITY;
-        for (int k = lane; k < S; k += 64) mx = fmaxf(mx, sw[h * kMaxSplits + k]);
+        for (int k = lane; k < S; k += 64) mx = fmaxf(mx, sw[k]);
         mx = wave_max(mx);
         float sum = 0.f;
         for (int k = lane; k < S; k += 64) {
-            const float mv = sw[h * kMaxSplits + k];
+            const float mv = sw[k];
             const float w = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - mx);
-            sw[h * kMaxSplits + k] = w;
-            sum = fmaf(w, sl[h * kMaxSplits + k], sum);
+            sw[k] = w;
+            sum = fmaf(w, sl[k], sum);
         }
         sum = wave_sum(sum);
-        if (lane == 0) sL[h] = sum;
+        if (lane == 0) sL = sum;
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, i = idx - (idx / D) * D;
-        const float* po = A.po + ((size_t)first * n_head_q + hq0 + h) * D + i;
-        const size_t step = (size_t)n_head_q * D;
-        const float* w = sw + h * kMaxSplits;
-        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-        int k = 0;
-        for (; k + 4 <= S; k += 4) {
-            o0 = fmaf(w[k], po[(size_t)k * step], o0);
-            o1 = fmaf(w[k + 1], po[(size_t)(k + 1) * step], o1);
-            o2 = fmaf(w[k + 2], po[(size_t)(k + 2) * step], o2);
-            o3 = fmaf(w[k + 3], po[(size_t)(k + 3) * step], o3);
-        }
-        for (; k < S; ++k) o0 = fmaf(w[k], po[(size_t)k * step], o0);
-        A.out[((size_t)s * n_head_q + hq0 + h) * D + i] = ((o0 + o1) + (o2 + o3)) / sL[h];
+    const size_t step = (size_t)n_head_q * D;
+    const float* po = A.po + ((size_t)first * n_head_q + hq) * D + i;
+    float acc[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+    int k = 0;
+    for (; k + 16 <= S; k += 16) {
+        float v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = po[(size_t)(k + u) * step];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = fmaf(sw[k + u], v[u], acc[u]);
     }
+    for (; k < S; ++k) acc[k & 15] = fmaf(sw[k], po[(size_t)k * step], acc[k & 15]);
+#pragma unroll
+    for (int u = 8; u >= 1; u >>= 1)
+#pragma unroll
+        for (int w = 0; w < u; ++w) acc[w] += acc[w + u];
+    A.out[((size_t)s * n_head_q + hq) * D + i] = acc[0] / sL;
 }
 
-__global__ void zero_kernel(uint4* p, size_t n16, uint32_t* tail, size_t n4tail) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t j = i; j < n16; j += stride) p[j] = make_uint4(0, 0, 0, 0);
-    for (size_t j = i; j < n4tail; j += stride) tail[j] = 0;
-}
+typedef void (*decode_fn)(const LaunchArgs);
+typedef void (*combine_fn)(const LaunchArgs, int32_t);
 
-typedef void (*kernel_fn)(const LaunchArgs);
-
-template <int D>
-kernel_fn pick_g(int G) {
+template <int D, int NW>
+decode_fn pick_g(int G) {
     switch (G) {
-        case 1: return decode_kernel<D, 1>;
-        case 2: return decode_kernel<D, 2>;
-        case 3: return decode_kernel<D, 3>;
-        case 4: return decode_kernel<D, 4>;
-        case 5: return decode_kernel<D, 5>;
-        case 6: return decode_kernel<D, 6>;
-        case 7: return decode_kernel<D, 7>;
-        case 8: return decode_kernel<D, 8>;
+        case 1: return decode_kernel<D, 1, NW>;
+        case 2: return decode_kernel<D, 2, NW>;
+        case 3: return decode_kernel<D, 3, NW>;
+        case 4: return decode_kernel<D, 4, NW>;
+        case 5: return decode_kernel<D, 5, NW>;
+        case 6: return decode_kernel<D, 6, NW>;
+        case 7: return decode_kernel<D, 7, NW>;
+        case 8: return decode_kernel<D, 8, NW>;
     }
     return nullptr;
 }
 
-kernel_fn pick_kernel(int D, int G) { return D == 128 ? pick_g<128>(G) : pick_g<64>(G); }
+decode_fn pick_decode(int D, int G, int NW) {
+    if (D == 128) return NW == 8 ? pick_g<128, 8>(G) : pick_g<128, 2>(G);
+    return NW == 8 ? pick_g<64, 8>(G) : pick_g<64, 2>(G);
+}
+
+combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
 }  // namespace
 }  // namespace kvd
@@ -621,23 +639,6 @@ extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* byt
     return KVD_OK;
 }
 
-extern "C" int kvd_attend_workspace_init(void* workspace, size_t bytes, void* stream) {
-    clear_error();
-    if (bytes == 0) return KVD_OK;
-    if (!workspace || (uintptr_t)workspace % 16) return fail(KVD_EINVAL, "workspace must be non-NULL and 16-byte aligned");
-    const size_t n16 = bytes / 16;
-    const size_t n4 = (bytes - n16 * 16) / 4;
-    uint32_t* tail = (uint32_t*)((uint8_t*)workspace + n16 * 16);
-    size_t blocks = (n16 + 255) / 256;
-    if (blocks < 1) blocks = 1;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)workspace, n16,
-                       tail, n4);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(KVD_EHIP, "workspace init launch: %s", hipGetErrorString(e));
-    return KVD_OK;
-}
-
 extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
     clear_error();
     AttendPlan p;
@@ -649,8 +650,9 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    const kernel_fn fn = pick_kernel(a->head_dim, p.group);
-    if (!fn) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
+    const decode_fn dk = pick_decode(a->head_dim, p.group, p.waves);
+    const combine_fn ck = pick_combine(a->head_dim);
+    if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 
     uint8_t* ws = (uint8_t*)a->workspace;
     const int D = a->head_dim;
@@ -690,7 +692,6 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
             L.pm = (float*)(ws + p.off_pm);
             L.pl = (float*)(ws + p.off_pl);
             L.po = (float*)(ws + p.off_po);
-            L.counters = (uint32_t*)(ws + p.off_counters) + (size_t)s0 * a->n_head_kv;
         }
         L.n_seq = ns;
         L.n_head_kv = a->n_head_kv;
@@ -699,9 +700,17 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
         L.split_off = (int32_t)base0;
         L.scale_log2e = scale_log2e;
         const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);
-        hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, L);
-        const hipError_t e = hipGetLastError();
+        hipLaunchKernelGGL(dk, dim3(grid), dim3(64 * p.waves), 0, (hipStream_t)stream, L);
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(KVD_EHIP, "decode kernel launch: %s", hipGetErrorString(e));
+        bool multi = false;
+        for (int j = 0; j < ns; ++j) multi |= L.seq[j].n_split > 1;
+        if (multi) {
+            hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q)), dim3(D), 0, (hipStream_t)stream, L,
+                               (int32_t)n_head_q);
+            e = hipGetLastError();
+            if (e != hipSuccess) return fail(KVD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
+        }
     }
     return KVD_OK;
 }

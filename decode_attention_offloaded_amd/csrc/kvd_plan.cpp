@@ -98,11 +98,15 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
+    // Waves per workgroup: 8 (one workgroup per CU, waves merged in LDS) once
+    // there are enough 64-row sub-tiles to give every wave of the chip one,
+    // else 2 (more, smaller workgroups for short contexts).
+    const int64_t work = total_sub * a->n_head_kv;
+    p->waves = (work >= kTargetWaves) ? 8 : 2;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
-        const int64_t work = total_sub * a->n_head_kv;
         const int64_t per_wave = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
-        split_rows = (int64_t)kSubRows * kWaves * per_wave;
+        split_rows = (int64_t)kSubRows * p->waves * per_wave;
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kSubRows) * kSubRows;
         split_rows = std::max(split_rows, floor_rows);
@@ -132,12 +136,10 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     if (base * a->n_head_kv >= ((int64_t)1 << 31) - 8) return fail(KVD_EINVAL, "too many work items");
 
     if (max_splits <= 1) {
-        p->off_counters = p->off_pm = p->off_pl = p->off_po = 0;
+        p->off_pm = p->off_pl = p->off_po = 0;
         p->ws_bytes = 0;
     } else {
         size_t off = 0;
-        p->off_counters = off;
-        off += round256((size_t)a->n_seq * a->n_head_kv * 4);
         p->off_pm = off;
         off += round256((size_t)base * a->n_head_q * 4);
         p->off_pl = off;

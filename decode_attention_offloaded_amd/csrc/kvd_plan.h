@@ -10,7 +10,6 @@
 
 namespace kvd {
 
-constexpr int kWaves = 2;               // waves per workgroup of the decode kernel
 constexpr int kSubRows = 64;            // rows per wave sub-tile (one row per lane)
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
 constexpr int64_t kTargetWaves = 2048;  // 256 CUs x 8 waves: enough sub-tiles to fill the chip
@@ -34,10 +33,11 @@ struct AttendPlan {
     int32_t group;        // G = n_head_q / n_head_kv
     int32_t chunk_bytes;  // bytes of one head of one row: head_dim / 32 * 34
     int32_t split_rows;
+    int32_t waves;        // waves per decode workgroup: 2, or 8 for large problems
     int32_t max_splits;   // largest per-sequence split count
     int64_t total_splits;
     std::vector<SeqPlan> seq;
-    size_t off_counters, off_pm, off_pl, off_po, ws_bytes;
+    size_t off_pm, off_pl, off_po, ws_bytes;  // workspace: split maxima, sums, outputs
 };
 
 // Validate every argument that does not need the GPU and build the plan.

@@ -76,8 +76,6 @@ def _declare(L):
     L.kvd_version.argtypes = []
     L.kvd_attend_workspace_bytes.restype = c_int
     L.kvd_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(c_size_t)]
-    L.kvd_attend_workspace_init.restype = c_int
-    L.kvd_attend_workspace_init.argtypes = [c_void_p, c_size_t, c_void_p]
     L.kvd_attend_decode.restype = c_int
     L.kvd_attend_decode.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
     L.kvd_ring_create.restype = c_void_p
@@ -181,7 +179,7 @@ def workspace_bytes(args: AttnArgs) -> int:
 
 
 class Workspace:
-    """Per-device scratch for split partials; zero-filled once, reused."""
+    """Per-device scratch for split partials, grown on demand and reused."""
 
     def __init__(self):
         self._buf = {}
@@ -193,7 +191,7 @@ class Workspace:
         key = torch.device(device).index
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             self._buf[key] = buf
         return buf
 

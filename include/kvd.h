@@ -88,9 +88,10 @@ const char* kvd_version(void);
  *
  * Work is split over (sequence, KV head, row range); each split keeps an
  * online-softmax partial and the partials of one (sequence, KV head) are
- * merged in a fixed order.  The split plan depends only on the shapes (never
- * on pointers, timing or the ring), so two calls with equal shapes and equal
- * input bytes give bit-identical outputs.
+ * merged in a fixed order by a second launch on the same stream.  The split
+ * plan depends only on the shapes (never on pointers, timing or the ring), so
+ * two calls with equal shapes and equal input bytes give bit-identical
+ * outputs.
  */
 typedef struct kvd_kv_seg {
     const void* k;       /* device: K row 0 of this segment (q8_0 rows) */
@@ -117,21 +118,17 @@ typedef struct kvd_attn_args {
     const kvd_kv_seg* segs;  /* HOST array [n_seq][n_seg]; read during the call only */
     const int64_t* q_pos;    /* HOST array [n_seq] of query positions, or NULL =
                                 the position of the last row of the last segment */
-    void* workspace;         /* device scratch owned by the caller, or NULL if
-                                kvd_attend_workspace_bytes reports 0 */
+    void* workspace;         /* device scratch owned by the caller (256-byte aligned),
+                                or NULL if kvd_attend_workspace_bytes reports 0 */
     size_t workspace_bytes;
 } kvd_attn_args;
 
 /* Bytes of workspace a call with these arguments needs (validates them too).
- * Returns KVD_OK and sets *bytes, or KVD_EINVAL. */
+ * Returns KVD_OK and sets *bytes, or KVD_EINVAL.  The workspace holds the split
+ * partials between the two launches of one call; it needs no initialisation.
+ * Calls that share a workspace must not overlap in time (use one stream, or
+ * order the streams). */
 int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
-
-/* Zero-fill a workspace on `stream` with a small kernel (no memset node).
- * A workspace must be zeroed once before its first use; every completed
- * kvd_attend_decode leaves it zeroed again where that matters (split
- * counters).  Calls that share a workspace must not overlap in time (use one
- * stream, or order the streams). */
-int kvd_attend_workspace_init(void* workspace, size_t bytes, void* stream);
 
 /* Enqueue decode attention on `stream` (asynchronous).  Returns KVD_OK,
  * KVD_EINVAL (bad shapes, unaligned or null pointers, a sequence with no

@@ -82,7 +82,7 @@ def test_workspace_plan():
     n = kvd.workspace_bytes(a)
     # 4096 rows x 8 KV heads = 512 sub-tiles of 64 rows: 128-row splits, 32 per head
     splits = 32
-    expect = 256 + 2 * ((splits * 40 * 4 + 255) // 256 * 256) + splits * 40 * 128 * 4
+    expect = 2 * ((splits * 40 * 4 + 255) // 256 * 256) + splits * 40 * 128 * 4
     assert n == expect
     short, _ = _args()
     short.segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 100, 0, 1088))
