@@ -146,35 +146,78 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
 # ---------------------------------------------------------------- host link + pipeline
 
 def link_peak(torch):
-    """Pinned host -> device copy bandwidth (GB/s) at several sizes; the peak is the plateau."""
+    """Pinned host -> device copy bandwidth (GB/s): one copy on one stream at
+    several sizes, and two equal copies on two streams at once (the ring's
+    configuration: K and V on their own DMA engines).  The peak is the best
+    plateau."""
     dev = torch.device("cuda:0")
     res = {}
-    s = torch.cuda.Stream(device=dev)
-    for mib in (1, 16, 64, 256, 1024):
-        n = mib << 20
-        h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
-        d = torch.empty(n, dtype=torch.uint8, device=dev)
+    s0, s1 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+
+    def run(n, streams):
+        hs = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in streams]
+        ds = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in streams]
         times = []
         for _ in range(6):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(s):
-                e0.record(s)
-                d.copy_(h, non_blocking=True)
-                e1.record(s)
             torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
+            t0 = time.perf_counter()
+            for s, h, d in zip(streams, hs, ds):
+                with torch.cuda.stream(s):
+                    d.copy_(h, non_blocking=True)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
         t = float(np.median(times[1:]))
-        res[str(mib)] = round(n / (t * 1e-3) / 1e9, 2)
-        del h, d
+        return round(n * len(streams) / t / 1e9, 2)
+
+    for mib in (1, 16, 64, 256):
+        res["1x%dMiB" % mib] = run(mib << 20, [s0])
+    for mib in (16, 64, 256):
+        res["2x%dMiB" % mib] = run(mib << 20, [s0, s1])
     return res
 
 
 def pipeline(args, torch, kvd, inputs):
+    """Host-resident 64-layer stack at 16384 rows: ordered (depth 0) vs pipelined
+    (depth 1, 128 MiB ring), against the pinned H2D link peak measured here."""
     from decode_attention_offloaded_amd import stack
+    link = link_peak(torch)
+    peak = max(link.values())
+    log("pinned H2D link: %s GB/s" % link)
     c = inputs.config(2)
     res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1),
-                                  budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=2, log=log)
+                                  budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log)
+    res["link_GBps_by_MiB"] = link
+    res["link_peak_GBps"] = peak
+    for arm in res["arms"].values():
+        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
     return res
+
+
+def long_context(args, torch, kvd, inputs):
+    """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
+    from decode_attention_offloaded_amd import stack
+    c = inputs.config(3)
+    out = {}
+    for budget_mib in (128, 1024):
+        r = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1, 2),
+                                    budget_bytes=budget_mib << 20, tokens=args.long_tokens, warmup=1, log=log,
+                                    distinct_layers=4)
+        out[str(budget_mib)] = r
+        log("long context, budget %d MiB: %s" % (budget_mib, {k: (v["ms_per_token"], v["declined"])
+                                                              for k, v in r["arms"].items()}))
+    return out
+
+
+def calibration_copy(torch, mib=256):
+    """A plain device-to-device copy of known size: the reference that hardware
+    fetch/write counters are scaled by when the traffic of the decode kernel is
+    measured with rocprofv3 --pmc (same process, same run)."""
+    n = mib << 20
+    a = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)  # one elementwise kernel: reads n bytes, writes n bytes
+    torch.cuda.synchronize()
+    return n
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -212,6 +255,26 @@ def cpu_baseline(target_s=15.0):
             "ms_per_layer": round(dt / reps * 1e3, 2)}
 
 
+def measured_traffic():
+    """HBM bytes per call from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    src = os.path.join(ROOT, "decode_attention_offloaded_amd", "csrc", "kvd_attend.hip")
+    prof = os.path.join(ROOT, "profiles", "decode_attention_4096rows_hbm_traffic.md")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        fields = {}
+        for line in open(prof):
+            if ":" in line and line.startswith("    "):
+                k, v = line.strip().split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel_source_sha256") == sha:
+            return int(fields["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +286,8 @@ def main():
     ap.add_argument("--pipe-layers", type=int, default=64)
     ap.add_argument("--pipe-tokens", type=int, default=8)
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
+    ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -232,6 +297,7 @@ def main():
     from decode_attention_offloaded_amd import inputs, kvd
     kvd.lib()
     log("device:", torch.cuda.get_device_name(0), kvd.version())
+    calib = calibration_copy(torch)
     d = device_resident(args, torch, kvd, inputs)
     log("device-resident: %.1f GB/s, %.3f us/launch" % (d["value"], d["us_per_launch"]))
     out = {
@@ -252,13 +318,16 @@ def main():
                    "n_ctx": 4096, "n_head_q": 40, "n_head_kv": 8, "head_dim": 128,
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel<128,5>", "bytes_per_launch": d["bytes_per_launch"],
-                     "us_per_launch": round(d["us_per_launch"], 3)},
+                     "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "decode_kernel<128,5,2> + combine_kernel<128> (one call)",
+                     "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
+        "calibration_copy_bytes": calib,
     }
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs)
+    if args.long:
+        out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

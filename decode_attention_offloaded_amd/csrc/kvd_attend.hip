@@ -317,8 +317,12 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
         const int row0 = r_begin + t * kSubRows;
         const int nv = min(kSubRows, r_end - row0);
         const bool has_next = t + NW < n_sub;
-        // next K in flight during this sub-tile's scores
-        if (has_next) load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + NW * kSubRows), toff, SG.stride);
+        // next K and V in flight during this sub-tile's scores and values
+        TileRegs<D> regs_v;
+        if (has_next) {
+            load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + NW * kSubRows), toff, SG.stride);
+            load_tile<D>(regs_v, tile_rsrc<D>(SG.v, SG, g, row0 + NW * kSubRows), toff, SG.stride);
+        }
         wave_lds_sync();
 
         // ---- scores, one lane per row
@@ -425,11 +429,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
             for (int h = 0; h < GP; h += 4) *(float4*)&pw[lane][h] = make_float4(pr[h], pr[h + 1], pr[h + 2], pr[h + 3]);
         }
         wave_lds_sync();
-        if (has_next) {
-            store_tile<D>(regs, tk, toff);
-            // next V in flight during this sub-tile's values
-            load_tile<D>(regs, tile_rsrc<D>(SG.v, SG, g, row0 + NW * kSubRows), toff, SG.stride);
-        }
+        if (has_next) store_tile<D>(regs, tk, toff);
 
         // ---- values, 16 dims per lane, RPP rows per pass
 #pragma unroll 2
@@ -465,7 +465,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
             }
         }
         wave_lds_sync();
-        if (has_next) store_tile<D>(regs, tv, toff);
+        if (has_next) store_tile<D>(regs_v, tv, toff);
     }
 
     // ---- wave state: total l; o summed over the row slots of each 16-lane

@@ -59,25 +59,34 @@ int Ring::find_layer(int32_t layer, int state) const {
     return -1;
 }
 
+void Ring::free_resources() {
+    for (Slot& s : slots_) {
+        if (s.k) t_->release(s.k);
+        if (s.v) t_->release(s.v);
+        for (EventH e : s.ready)
+            if (e) t_->event_destroy(e);
+        if (s.rel) t_->event_destroy(s.rel);
+    }
+    slots_.clear();
+    for (StreamH& x : xfer_) {
+        if (x) t_->stream_destroy(x);
+        x = nullptr;
+    }
+}
+
 int Ring::engage(int64_t slot_bytes) {
     slots_.assign(n_slots_, Slot());
-    bool ok = t_->stream_create(&xfer_) == 0;
+    bool ok = true;
+    for (StreamH& x : xfer_) ok = ok && t_->stream_create(&x) == 0;
     for (int i = 0; ok && i < n_slots_; ++i) {
         Slot& s = slots_[i];
-        ok = t_->event_create(&s.ready) == 0 && t_->event_create(&s.rel) == 0 &&
-             t_->alloc((size_t)slot_bytes, &s.k) == 0 && t_->alloc((size_t)slot_bytes, &s.v) == 0;
+        for (EventH& e : s.ready) ok = ok && t_->event_create(&e) == 0;
+        ok = ok && t_->event_create(&s.rel) == 0 && t_->alloc((size_t)slot_bytes, &s.k) == 0 &&
+             t_->alloc((size_t)slot_bytes, &s.v) == 0;
     }
     if (!ok) {
         // a failed allocation is a decline, not an error: undo everything
-        for (Slot& s : slots_) {
-            if (s.k) t_->release(s.k);
-            if (s.v) t_->release(s.v);
-            if (s.ready) t_->event_destroy(s.ready);
-            if (s.rel) t_->event_destroy(s.rel);
-        }
-        slots_.clear();
-        if (xfer_) t_->stream_destroy(xfer_);
-        xfer_ = nullptr;
+        free_resources();
         return KVD_ENOMEM;
     }
     engaged_ = true;
@@ -90,18 +99,11 @@ int Ring::engage(int64_t slot_bytes) {
 
 void Ring::teardown() {
     if (!engaged_) return;
-    if (xfer_) t_->stream_sync(xfer_);
+    for (StreamH x : xfer_)
+        if (x) t_->stream_sync(x);
     for (Slot& s : slots_)
         if (s.released_once && s.rel) t_->event_sync(s.rel);
-    for (Slot& s : slots_) {
-        if (s.k) t_->release(s.k);
-        if (s.v) t_->release(s.v);
-        if (s.ready) t_->event_destroy(s.ready);
-        if (s.rel) t_->event_destroy(s.rel);
-    }
-    slots_.clear();
-    if (xfer_) t_->stream_destroy(xfer_);
-    xfer_ = nullptr;
+    free_resources();
     engaged_ = false;
     slot_bytes_ = 0;
     cursor_ = 0;
@@ -152,15 +154,18 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
         return fail(KVD_ESTATE,
                     "slot %d still holds layer %d: release it before staging layer %d (look-ahead deeper than the ring)",
                     s, S.layer, a->layer);
-    // stream to stream: the copy waits for the release of the slot's previous
+    // stream to stream: the copies wait for the release of the slot's previous
     // layer, recorded earlier in host order on the compute stream
-    if (S.released_once && t_->wait(xfer_, S.rel) != 0) return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
     const size_t bytes = (size_t)rows * (size_t)a->row_bytes;
-    if (bytes > 0) {
-        if (t_->copy_h2d(S.k, a->host_k, bytes, xfer_) != 0 || t_->copy_h2d(S.v, a->host_v, bytes, xfer_) != 0)
+    void* dst[kXferStreams] = {S.k, S.v};
+    const void* src[kXferStreams] = {a->host_k, a->host_v};
+    for (int x = 0; x < kXferStreams; ++x) {
+        if (S.released_once && t_->wait(xfer_[x], S.rel) != 0)
+            return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
+        if (bytes > 0 && t_->copy_h2d(dst[x], src[x], bytes, xfer_[x]) != 0)
             return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
+        if (t_->record(S.ready[x], xfer_[x]) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
     }
-    if (t_->record(S.ready, xfer_) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
     S.state = STAGED;
     S.layer = a->layer;
     S.prefix_rows = rows;
@@ -239,10 +244,10 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
             const void* hk = (const uint8_t*)a->host_k + off;
             const void* hv = (const uint8_t*)a->host_v + off;
             if (last_xfer_ == S.delivery + 1) {
-                // this layer's prefix is the newest work on the transfer stream:
+                // this layer's prefix is the newest work on the transfer streams:
                 // the tail follows it there and `ready` moves behind the tail
-                if (t_->copy_h2d(dk, hk, n, xfer_) != 0 || t_->copy_h2d(dv, hv, n, xfer_) != 0 ||
-                    t_->record(S.ready, xfer_) != 0)
+                if (t_->copy_h2d(dk, hk, n, xfer_[0]) != 0 || t_->record(S.ready[0], xfer_[0]) != 0 ||
+                    t_->copy_h2d(dv, hv, n, xfer_[1]) != 0 || t_->record(S.ready[1], xfer_[1]) != 0)
                     return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
             } else {
                 // later prefixes are queued on the transfer stream: do not wait
@@ -255,7 +260,8 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
         st_.n_acquire_pipelined++;
     }
     Slot& S = slots_[s];
-    if (t_->wait(compute, S.ready) != 0) return fail(KVD_EHIP, "wait(ready): %s", t_->error_text());
+    for (EventH e : S.ready)
+        if (t_->wait(compute, e) != 0) return fail(KVD_EHIP, "wait(ready): %s", t_->error_text());
     S.state = ACQUIRED;
     if (out) *out = kvd_slot_view{S.k, S.v, a->n_rows, a->row_bytes, 1, s};
     return KVD_OK;

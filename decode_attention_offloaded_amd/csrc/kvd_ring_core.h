@@ -49,6 +49,11 @@ public:
 // Returns false on overflow.  Depth 0 has no ring (need = 0).
 bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t* need);
 
+// Transfer streams per ring: K rows go on one, V rows on the other, so two
+// DMA engines copy in parallel (one engine tops out below the host link, and
+// engines differ in speed).
+constexpr int kXferStreams = 2;
+
 class Ring {
 public:
     Ring(std::unique_ptr<Transport> t, int32_t depth, int64_t budget);
@@ -65,7 +70,7 @@ private:
     struct Slot {
         void* k = nullptr;
         void* v = nullptr;
-        EventH ready = nullptr;
+        EventH ready[kXferStreams] = {nullptr, nullptr};  // one per transfer stream
         EventH rel = nullptr;
         int state = FREE;
         int32_t layer = -1;
@@ -82,6 +87,7 @@ private:
     // (ring usable), KVD_DECLINED (ordered path), or an error.
     int plan(const kvd_stage_args* a);
     int engage(int64_t slot_bytes);
+    void free_resources();
     bool busy() const;  // any slot STAGED or ACQUIRED
     int find_layer(int32_t layer, int state) const;
     int deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out);
@@ -96,7 +102,7 @@ private:
     int device_ = -1;
     int64_t slot_bytes_ = 0;  // bytes per K (and per V) buffer of a slot
     int64_t need_ = 0;
-    StreamH xfer_ = nullptr;
+    StreamH xfer_[kXferStreams] = {nullptr, nullptr};
     std::vector<Slot> slots_;
     uint64_t cursor_ = 0;        // deliveries issued so far
     uint64_t last_xfer_ = 0;     // cursor+1 of the delivery last put on the transfer stream (0 = none)

@@ -165,6 +165,7 @@ class Stack:
     def close(self):
         self.stream.synchronize()
         self.ring.close()
+        self.ring = None
 
 
 def cfg_q(g, cfg):
@@ -185,7 +186,7 @@ def token_rows(cfg, pool: int = 4):
 
 
 def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budget_bytes=128 << 20, tokens=8,
-                      warmup=2, log=print, n_rows=None, gemv=True, distinct_layers=None):
+                      warmup=3, log=print, n_rows=None, gemv=True, distinct_layers=None):
     """Ordered vs pipelined per-token time for a host-resident stack, arms run
     A/B/B/A (reversed order on the second pass).  Returns a dict for the bench."""
     n_rows = n_rows or cfg.n_ctx
@@ -203,13 +204,18 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
                    for _ in range(n_layers)]
     rows_fn = token_rows(cfg)
     order = list(depths) + list(reversed(depths))
+    # One compute stream for every arm, as an engine has one: streams share the
+    # process's few hardware queues, and a fresh stream per arm would make the
+    # queue a transfer stream lands on (and so the overlap) vary between arms.
+    compute = torch.cuda.Stream(device=dev)
     times = {d: [] for d in depths}
     outs, stats, vram = {}, {}, {}
     for d in order:
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         free0 = torch.cuda.mem_get_info(dev)[0]
-        st = Stack(torch, kvd, cfg, host, n_rows, d, budget_bytes, gemv_weights=weights, new_rows=rows_fn)
+        st = Stack(torch, kvd, cfg, host, n_rows, d, budget_bytes, gemv_weights=weights, new_rows=rows_fn,
+                   stream=compute)
         for t in range(warmup):
             st.token(t)
         free1 = torch.cuda.mem_get_info(dev)[0]

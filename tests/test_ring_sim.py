@@ -257,7 +257,7 @@ def test_lazy_transport(sim_lib):
     h = Harness(sim_lib, 2, 1 << 40, 5, 16)
     assert h.counter(STREAMS) == 0 and h.counter(PEAK) == 0
     h.token(16)
-    assert h.counter(STREAMS) == 1
+    assert h.counter(STREAMS) == 2   # K and V transfer streams
     h.close()
 
 
