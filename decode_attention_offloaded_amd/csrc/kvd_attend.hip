@@ -538,65 +538,358 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
     }
 }
 
-// Merge the split partials of one (sequence, query head) in split order: one
-// workgroup per (sequence, query head), one thread per dimension.  The split
-// maxima and sums go through LDS once; each thread then keeps 16 independent
-// loads of partial outputs in flight.  A separate launch, so the partials
-// written by the decode kernel are visible without cache maintenance inside a
-// kernel.
+// ---------------------------------------------------------------------------
+// Block-sliced form of the decode kernel (the default).  A workgroup has one
+// wave per q8_0 block of the head (D / 32 waves) and walks the split's rows
+// in 64-row tiles, all waves on the same tile:
+//   * wave w loads only block w of each row (a 9-dword window around its 34
+//     bytes) for K and V, one tile ahead in registers, staged through a
+//     wave-private LDS tile;
+//   * scores: one lane per row, the block's 32 codes against the query slice
+//     (scalar registers, read 4 dims x G heads at a time), times the block
+//     scale; the D / 32 block partials meet in LDS at one workgroup barrier
+//     per tile (LDS-only fences, so the prefetch stays in flight), and every
+//     wave sums them in the same order, so all waves hold identical scores;
+//   * online softmax, repeated identically in each wave: the running maximum
+//     is only raised when a score passes it by more than kLazyMax (log2
+//     units), so most tiles need no wave-wide maximum and no rescale;
+//   * values: wave w accumulates the 32 dims of block w; a lane holds 4 dims
+//     (G x 4 accumulators) and 8 consecutive lanes take 8 rows of a pass;
+//   * at the end each wave folds its 8 row slots (three DPP steps) and writes
+//     its 32 dims: the waves own disjoint dims, so no cross-wave merge.
+constexpr float kLazyMax = 8.0f;
+
+// First dword of the 9-dword window holding block b of a head chunk, and the
+// byte offset of the block's scale within that window (0 or 2).
+__device__ inline int win_dword(int b) { return (34 * b) >> 2; }
+
+template <int D, int G>
+struct Slice {
+    static constexpr int NB = D / 32;        // waves per workgroup
+    static constexpr int GP = (G + 3) / 4 * 4;
+    static constexpr int T = 64;             // rows per tile
+    static constexpr int W = 9;              // dwords per row window
+};
+
+__device__ inline void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Window loads: instruction i of 9 reads unit 64 i + lane of the tile's
+// 64 x 9 dwords (row = unit / 9, dword = unit % 9), so the LDS copy is a
+// plain lane-contiguous store and each instruction covers ~7 rows of 36
+// contiguous bytes.
+__device__ inline void load_win(uint32_t (&r)[9], __amdgpu_buffer_rsrc_t rs, const int32_t (&voff)[9]) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0);
+}
+
+__device__ inline void store_win(const uint32_t (&r)[9], uint32_t* t, int lane) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i) t[64 * i + lane] = r[i];
+}
+
+template <int D, int G, int ODD>
+__device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int g,
+                                           const int r_begin, const int r_end, const bool single,
+                                           const int abs_split, const int wave, const int lane, uint32_t* tk,
+                                           uint32_t* tv, float* sx, float* scw) {
+    using S_ = Slice<D, G>;
+    constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
+    const int n_tiles = (r_end - r_begin + T - 1) / T;
+    const int n_head_q = A.n_head_kv * G;
+    const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
+
+    int32_t voff[9];
+    {
+        const int32_t base = win_dword(wave) * 4;
+#pragma unroll
+        for (int i = 0; i < 9; ++i) {
+            const int u = i + lane;
+            voff[i] = (7 * i + u / 9) * SG.stride + (u % 9) * 4 + base;
+        }
+    }
+
+    float m[G], l[G], o[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
+    }
+    const int slot = lane & 7;   // value phase: row slot (8 consecutive lanes = 8 rows)
+    const int grp = lane >> 3;   // value phase: 4-dim group within the block
+
+    // K of a tile is staged before its scores, V only after them, so the
+    // scores of the first tile start as soon as its K has arrived; the next
+    // tile's K and V are in flight in registers meanwhile.
+    uint32_t rk[9], rv[9];
+    load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
+    load_win(rv, tile_rsrc<D>(SG.v, SG, g, r_begin), voff);
+    warm_query<G * D>(qg - 32 * wave);
+    store_win(rk, tk, lane);
+
+    for (int t = 0; t < n_tiles; ++t) {
+        const int row0 = r_begin + t * T;
+        const int nv = min(T, r_end - row0);
+        const bool has_next = t + 1 < n_tiles;
+        if (has_next) load_win(rk, tile_rsrc<D>(SG.k, SG, g, row0 + T), voff);
+        wave_lds_sync();
+
+        // ---- block partial scores, one lane per row
+        float* sxt = sx + (t & 1) * (NB * G * 64);
+        {
+            const uint32_t* rp = tk + lane * 9;
+            uint32_t w[9];
+#pragma unroll
+            for (int j = 0; j < 9; ++j) w[j] = rp[j];
+            float4 qc[G];
+            {
+                const_f32_ptr qp = (const_f32_ptr)qg;
+                asm volatile("" : "+s"(qp));
+#pragma unroll
+                for (int h = 0; h < G; ++h) qc[h] = ldq4(qp + h * D);
+            }
+            float dot[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) dot[h] = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
+                float4 qn[G];
+                if (c + 1 < 8) {
+                    const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
+                    asm volatile("" : "+s"(qp));
+#pragma unroll
+                    for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
+                }
+                const uint32_t x = ODD ? w[c + 1] : __builtin_amdgcn_alignbyte(w[c + 1], w[c], 2);
+                const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    dot[h] = fmaf(qc[h].x, k0, dot[h]);
+                    dot[h] = fmaf(qc[h].y, k1, dot[h]);
+                    dot[h] = fmaf(qc[h].z, k2, dot[h]);
+                    dot[h] = fmaf(qc[h].w, k3, dot[h]);
+                }
+                if (c + 1 < 8) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) qc[h] = qn[h];
+                }
+            }
+            const float dk = ODD ? half_hi(w[0]) : half_lo(w[0]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) sxt[(wave * G + h) * 64 + lane] = dot[h] * dk;
+        }
+        lds_barrier();
+        store_win(rv, tv, lane);
+        if (has_next) load_win(rv, tile_rsrc<D>(SG.v, SG, g, row0 + T), voff);
+        wave_lds_sync();
+
+        // ---- full scores (same sum order in every wave) and online softmax
+        float sc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float a = sxt[h * 64 + lane];
+#pragma unroll
+            for (int b = 1; b < NB; ++b) a += sxt[(b * G + h) * 64 + lane];
+            sc[h] = (lane < nv) ? a * A.scale_log2e : -INFINITY;
+        }
+        {
+            bool big = false;
+#pragma unroll
+            for (int h = 0; h < G; ++h) big |= sc[h] > m[h] + kLazyMax;
+            if (__builtin_amdgcn_ballot_w64(big)) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mn = fmaxf(m[h], wave_max(sc[h]));
+                    if (mn > m[h]) {
+                        const float alpha = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+                        l[h] *= alpha;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) o[h][e] *= alpha;
+                        m[h] = mn;
+                    }
+                }
+            }
+        }
+        {
+            // rows past the visible range may hold any bits: their weight is an exact 0
+            const float dv = (lane < nv) ? (ODD ? half_hi(tv[lane * 9]) : half_lo(tv[lane * 9])) : 0.f;
+            float c[GP];
+#pragma unroll
+            for (int h = 0; h < GP; ++h) c[h] = 0.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
+                l[h] += p;
+                c[h] = p * dv;
+            }
+#pragma unroll
+            for (int h = 0; h < GP; h += 4) *(float4*)&scw[lane * GP + h] = make_float4(c[h], c[h + 1], c[h + 2], c[h + 3]);
+        }
+        wave_lds_sync();
+
+        // ---- values: 4 dims per lane, 8 rows per pass
+#pragma unroll 4
+        for (int ps = 0; ps < 8; ++ps) {
+            const int r = ps * 8 + slot;
+            const uint32_t* rp = tv + r * 9;
+            const uint32_t x = ODD ? rp[grp + 1] : __builtin_amdgcn_alignbyte(rp[grp + 1], rp[grp], 2);
+            float c[GP];
+#pragma unroll
+            for (int h = 0; h < GP; h += 4) {
+                const float4 cv = *(const float4*)&scw[r * GP + h];
+                c[h] = cv.x;
+                c[h + 1] = cv.y;
+                c[h + 2] = cv.z;
+                c[h + 3] = cv.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float vv = sbyte(x, e);
+#pragma unroll
+                for (int h = 0; h < G; ++h) o[h][e] = fmaf(c[h], vv, o[h][e]);
+            }
+        }
+        wave_lds_sync();
+        if (has_next) store_win(rk, tk, lane);
+    }
+
+    // ---- fold the 8 row slots (same m in every slot; 8 consecutive lanes), finish l
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = o[h][e];
+            x += dpp<kDppQuadXor1>(x);
+            x += dpp<kDppQuadXor2>(x);
+            x += dpp<kDppRowHalfMirror>(x);
+            o[h][e] = x;
+        }
+        l[h] = wave_sum(l[h]);
+    }
+    const int hq0 = g * G;
+    const int dim0 = 32 * wave + 4 * grp;
+    if (slot == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if (single) {
+                const float inv = 1.f / l[h];
+                *(float4*)&A.out[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
+                    make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
+            } else {
+                const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
+                *(float4*)&A.po[pi * D + dim0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+            }
+        }
+    }
+    if (!single && wave == 0 && lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
+            A.pm[pi] = m[h];
+            A.pl[pi] = l[h];
+        }
+    }
+}
+
+template <int D, int G>
+__global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A) {
+    using S_ = Slice<D, G>;
+    constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
+    __shared__ __attribute__((aligned(16))) uint32_t s_kv[NB][2][T * 9];
+    __shared__ __attribute__((aligned(16))) float s_x[2 * NB * G * 64];
+    __shared__ __attribute__((aligned(16))) float s_c[NB][T * GP];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nblk = gridDim.x;
+    const int item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    if (item >= A.n_items) return;
+    const int lsplit = item / A.n_head_kv;
+    const int g = item - lsplit * A.n_head_kv;
+    int s = 0;
+    while (s + 1 < A.n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
+    const SeqDesc& SQ = A.seq[s];
+    int sp = lsplit - SQ.split_base;
+    int sgi = 0;
+    if (sp >= SQ.seg[0].n_split) {
+        sp -= SQ.seg[0].n_split;
+        sgi = 1;
+    }
+    const SegDesc& SG = SQ.seg[sgi];
+    const int r_begin = SG.row_lo + sp * A.split_rows;
+    const int r_end = min(r_begin + A.split_rows, SG.row_lo + SG.n_vis);
+    const bool single = SQ.n_split == 1;
+    const int abs_split = A.split_off + lsplit;
+    if (wave & 1)
+        slice_body<D, G, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+                            s_kv[wave][1], s_x, s_c[wave]);
+    else
+        slice_body<D, G, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+                            s_kv[wave][1], s_x, s_c[wave]);
+}
+
+// Merge the split partials of one (sequence, query head) in split order.  One
+// workgroup per (sequence, query head), one wave per 32 dims; lanes take
+// splits, 64 at a time.  Every lane loads its split's maximum, sum and 32
+// partial outputs together (one round trip), the weights follow from a wave
+// maximum, and the 64 weighted rows are summed column by column through LDS,
+// in split order, so the result does not depend on timing.  A separate
+// launch, so the partials written by the decode kernel are visible without
+// cache maintenance inside a kernel.
 template <int D>
-__global__ void __launch_bounds__(D) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
-    __shared__ float sw[kMaxSplits];  // maxima, then weights
-    __shared__ float sl[kMaxSplits];  // partial sums
-    __shared__ float sL;
-    const int i = threadIdx.x;
-    const int lane = i & 63;
+__global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
+    constexpr int NWV = D / 32;
+    __shared__ float s_o[NWV][64][33];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hq = blockIdx.x % n_head_q;
     const int s = blockIdx.x / n_head_q;
     const SeqDesc& SQ = A.seq[s];
     const int S = SQ.n_split;
     if (S <= 1) return;  // written directly by the decode kernel
     const int first = A.split_off + SQ.split_base;
-    for (int k = i; k < S; k += D) {
-        const size_t pi = (size_t)(first + k) * n_head_q + hq;
-        sw[k] = A.pm[pi];
-        sl[k] = A.pl[pi];
-    }
-    __syncthreads();
-    if (i < 64) {
-        float mx = -INFINITY;
-        for (int k = lane; k < S; k += 64) mx = fmaxf(mx, sw[k]);
-        mx = wave_max(mx);
-        float sum = 0.f;
-        for (int k = lane; k < S; k += 64) {
-            const float mv = sw[k];
-            const float w = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - mx);
-            sw[k] = w;
-            sum = fmaf(w, sl[k], sum);
+    float(*so)[33] = s_o[wave];
+    float M = -INFINITY, L = 0.f, acc = 0.f;  // acc: dimension 32 * wave + lane (lanes < 32)
+    for (int c0 = 0; c0 < S; c0 += 64) {
+        const int k = c0 + lane;
+        const bool ok = k < S;
+        const size_t pi = (size_t)(first + (ok ? k : c0)) * n_head_q + hq;
+        const float pm = ok ? A.pm[pi] : -INFINITY;
+        const float pl = ok ? A.pl[pi] : 0.f;
+        const float4* po = (const float4*)(A.po + pi * D + 32 * wave);
+        float4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = po[j];
+        const float Mn = fmaxf(M, wave_max(pm));
+        const float w = ok ? __builtin_amdgcn_exp2f(pm - Mn) : 0.f;
+        const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        L = fmaf(L, alpha, wave_sum(w * pl));
+        acc *= alpha;
+        M = Mn;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            so[lane][4 * j] = w * v[j].x;
+            so[lane][4 * j + 1] = w * v[j].y;
+            so[lane][4 * j + 2] = w * v[j].z;
+            so[lane][4 * j + 3] = w * v[j].w;
         }
-        sum = wave_sum(sum);
-        if (lane == 0) sL = sum;
+        wave_lds_sync();
+        if (lane < 32) {
+            float t = 0.f;
+#pragma unroll 16
+            for (int r = 0; r < 64; ++r) t += so[r][lane];
+            acc += t;
+        }
+        wave_lds_sync();
     }
-    __syncthreads();
-    const size_t step = (size_t)n_head_q * D;
-    const float* po = A.po + ((size_t)first * n_head_q + hq) * D + i;
-    float acc[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = 0.f;
-    int k = 0;
-    for (; k + 16 <= S; k += 16) {
-        float v[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = po[(size_t)(k + u) * step];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] = fmaf(sw[k + u], v[u], acc[u]);
-    }
-    for (; k < S; ++k) acc[k & 15] = fmaf(sw[k], po[(size_t)k * step], acc[k & 15]);
-#pragma unroll
-    for (int u = 8; u >= 1; u >>= 1)
-#pragma unroll
-        for (int w = 0; w < u; ++w) acc[w] += acc[w + u];
-    A.out[((size_t)s * n_head_q + hq) * D + i] = acc[0] / sL;
+    if (lane < 32) A.out[((size_t)s * n_head_q + hq) * D + 32 * wave + lane] = acc / L;
 }
 
 typedef void (*decode_fn)(const LaunchArgs);
@@ -624,6 +917,23 @@ decode_fn pick_decode(int D, int G, int NW) {
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
+template <int D>
+decode_fn pick_slice_g(int G) {
+    switch (G) {
+        case 1: return slice_kernel<D, 1>;
+        case 2: return slice_kernel<D, 2>;
+        case 3: return slice_kernel<D, 3>;
+        case 4: return slice_kernel<D, 4>;
+        case 5: return slice_kernel<D, 5>;
+        case 6: return slice_kernel<D, 6>;
+        case 7: return slice_kernel<D, 7>;
+        case 8: return slice_kernel<D, 8>;
+    }
+    return nullptr;
+}
+
+decode_fn pick_slice(int D, int G) { return D == 128 ? pick_slice_g<128>(G) : pick_slice_g<64>(G); }
+
 }  // namespace
 }  // namespace kvd
 
@@ -650,7 +960,7 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    const decode_fn dk = pick_decode(a->head_dim, p.group, p.waves);
+    const decode_fn dk = p.kernel == 3 ? pick_slice(a->head_dim, p.group) : pick_decode(a->head_dim, p.group, p.waves);
     const combine_fn ck = pick_combine(a->head_dim);
     if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 
@@ -706,7 +1016,7 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
         bool multi = false;
         for (int j = 0; j < ns; ++j) multi |= L.seq[j].n_split > 1;
         if (multi) {
-            hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q)), dim3(D), 0, (hipStream_t)stream, L,
+            hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q)), dim3(2 * D), 0, (hipStream_t)stream, L,
                                (int32_t)n_head_q);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(KVD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));

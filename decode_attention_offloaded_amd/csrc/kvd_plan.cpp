@@ -98,18 +98,24 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
-    // Waves per workgroup: 8 (one workgroup per CU, waves merged in LDS) once
-    // there are enough 64-row sub-tiles to give every wave of the chip one,
-    // else 2 (more, smaller workgroups for short contexts).
+    // Kernel and waves per workgroup.  Up to kSliceMaxWork tile-heads the
+    // block-sliced kernel (one wave per q8_0 block, D / 32 waves sharing each
+    // tile: short per-wave chains for short contexts); beyond, the lane-per-row
+    // kernel with 8 waves (one workgroup per CU, waves merged in LDS), whose
+    // longer splits keep the merge small.
     const int64_t work = total_sub * a->n_head_kv;
-    p->waves = (work >= kTargetWaves) ? 8 : 2;
+    p->kernel = kKernelChoice != 0 ? kKernelChoice : (work <= kSliceMaxWork ? 3 : 1);
+    p->waves = p->kernel == 3 ? a->head_dim / 32 : (work >= kTargetWaves) ? 8 : 2;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
         const int64_t per_wave = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
-        split_rows = (int64_t)kSubRows * p->waves * per_wave;
+        // block-sliced: all waves of a workgroup share each 64-row tile
+        split_rows = (int64_t)kSubRows * (p->kernel == 3 ? 1 : p->waves) * per_wave;
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kSubRows) * kSubRows;
         split_rows = std::max(split_rows, floor_rows);
+        // up to kOneSplitRows visible rows per sequence: one split, no combine launch
+        if (max_vis <= kOneSplitRows) split_rows = std::max<int64_t>(split_rows, ceil_div(max_vis, kSubRows) * kSubRows);
         if (split_rows > (1 << 24)) split_rows = 1 << 24;
     }
     p->split_rows = (int32_t)split_rows;
