@@ -115,16 +115,18 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
         r = np.random.default_rng([c.seed, 1000 + i, n])
         ks.append(torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev))
         vs.append(torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev))
-    q = torch.from_numpy(inputs.random_q(np.random.default_rng(n), 1, c.n_head_q, c.head_dim)).to(dev)
-    out = torch.empty_like(q)
+    # a query per layer, as in a decode step (a query reused across calls stays cached)
+    qs = [torch.from_numpy(inputs.random_q(np.random.default_rng([n, i]), 1, c.n_head_q, c.head_dim)).to(dev)
+          for i in range(reps)]
+    out = torch.empty_like(qs[0])
     with torch.cuda.stream(stream):
         for i in range(reps):
-            kvd.attend_decode(q, out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+            kvd.attend_decode(qs[i], out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for i in range(reps):
-            kvd.attend_decode(q, out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
+            kvd.attend_decode(qs[i], out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -176,11 +178,10 @@ def link_peak(torch):
     return res
 
 
-def pipeline(args, torch, kvd, inputs):
+def pipeline(args, torch, kvd, inputs, link):
     """Host-resident 64-layer stack at 16384 rows: ordered (depth 0) vs pipelined
     (depth 1, 128 MiB ring), against the pinned H2D link peak measured here."""
     from decode_attention_offloaded_amd import stack
-    link = link_peak(torch)
     peak = max(link.values())
     log("pinned H2D link: %s GB/s" % link)
     c = inputs.config(2)
@@ -190,6 +191,24 @@ def pipeline(args, torch, kvd, inputs):
     res["link_peak_GBps"] = peak
     for arm in res["arms"].values():
         arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    return res
+
+
+def batched(args, torch, kvd, inputs, link):
+    """16 sequences of lognormal lengths, 64 layers (odd layers: 4096-row window),
+    older half of every sequence staged from pinned host memory through a
+    depth-1 ring (1 GiB budget), newer half device-resident: ordered vs
+    pipelined per-token time."""
+    from decode_attention_offloaded_amd import batched as bt
+    c = inputs.config(4)
+    res = bt.run_batched(torch, kvd, inputs, c, n_layers=args.batched_layers, depths=(0, 1),
+                         budget_bytes=1 << 30, tokens=args.batched_tokens, warmup=2, log=log,
+                         distinct_layers=4)
+    peak = max(link.values())
+    res["link_peak_GBps"] = peak
+    for arm in res["arms"].values():
+        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    log("batched: %s" % {k: (v["ms_per_token"], v["staged_GBps"]) for k, v in res["arms"].items()})
     return res
 
 
@@ -286,6 +305,9 @@ def main():
     ap.add_argument("--pipe-layers", type=int, default=64)
     ap.add_argument("--pipe-tokens", type=int, default=8)
     ap.add_argument("--cpu-baseline", type=int, default=1)
+    ap.add_argument("--batched", type=int, default=1, help="run the 16-sequence mixed-residency stack")
+    ap.add_argument("--batched-layers", type=int, default=64)
+    ap.add_argument("--batched-tokens", type=int, default=4)
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
@@ -319,13 +341,16 @@ def main():
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "decode_kernel<128,5,2> + combine_kernel<128> (one call)",
+                     "kernel": "slice_kernel<128,5> + combine_kernel<128> (one call)",
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
         "calibration_copy_bytes": calib,
     }
+    link = link_peak(torch) if (args.pipeline or args.batched) else None
     if args.pipeline:
-        out["pipeline"] = pipeline(args, torch, kvd, inputs)
+        out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
+    if args.batched:
+        out["batched"] = batched(args, torch, kvd, inputs, link)
     if args.long:
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:

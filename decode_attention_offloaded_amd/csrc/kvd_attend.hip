@@ -546,7 +546,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
 //     bytes) for K and V, one tile ahead in registers, staged through a
 //     wave-private LDS tile;
 //   * scores: one lane per row, the block's 32 codes against the query slice
-//     (scalar registers, read 4 dims x G heads at a time), times the block
+//     (staged in LDS, read back 4 dims x G heads at a time), times the block
 //     scale; the D / 32 block partials meet in LDS at one workgroup barrier
 //     per tile (LDS-only fences, so the prefetch stays in flight), and every
 //     wave sums them in the same order, so all waves hold identical scores;
@@ -595,7 +595,7 @@ template <int D, int G, int ODD>
 __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int g,
                                            const int r_begin, const int r_end, const bool single,
                                            const int abs_split, const int wave, const int lane, uint32_t* tk,
-                                           uint32_t* tv, float* sx, float* scw) {
+                                           uint32_t* tv, float* sx, float* scw, float* sq) {
     using S_ = Slice<D, G>;
     constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
     const int n_tiles = (r_end - r_begin + T - 1) / T;
@@ -626,10 +626,16 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     // K of a tile is staged before its scores, V only after them, so the
     // scores of the first tile start as soon as its K has arrived; the next
     // tile's K and V are in flight in registers meanwhile.
+    // The wave's query slice (G heads x 32 dims) goes to LDS with one vector
+    // load per lane, issued first; the scores read it back as wave-uniform
+    // float4s.  (Scalar loads of a query that is cold in the scalar cache
+    // serialise on its misses: several microseconds per call.)
+    float4 qv4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane < G * 8) qv4 = *(const float4*)(qg + (lane >> 3) * D + 4 * (lane & 7));
     uint32_t rk[9], rv[9];
     load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
     load_win(rv, tile_rsrc<D>(SG.v, SG, g, r_begin), voff);
-    warm_query<G * D>(qg - 32 * wave);
+    if (lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
     store_win(rk, tk, lane);
 
     for (int t = 0; t < n_tiles; ++t) {
@@ -646,12 +652,15 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             uint32_t w[9];
 #pragma unroll
             for (int j = 0; j < 9; ++j) w[j] = rp[j];
+            // query chunks of 4 dims x G heads from LDS, one chunk ahead; the
+            // empty asm statements keep the reads from being hoisted (and the
+            // query from occupying more than two chunks of registers)
             float4 qc[G];
             {
-                const_f32_ptr qp = (const_f32_ptr)qg;
-                asm volatile("" : "+s"(qp));
+                int off = 0;
+                asm volatile("" : "+v"(off));
 #pragma unroll
-                for (int h = 0; h < G; ++h) qc[h] = ldq4(qp + h * D);
+                for (int h = 0; h < G; ++h) qc[h] = *(const float4*)&sq[h * 32 + off];
             }
             float dot[G];
 #pragma unroll
@@ -662,10 +671,10 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
                 for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
                 float4 qn[G];
                 if (c + 1 < 8) {
-                    const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
-                    asm volatile("" : "+s"(qp));
+                    int off = 4 * (c + 1);
+                    asm volatile("" : "+v"(off));
 #pragma unroll
-                    for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
+                    for (int h = 0; h < G; ++h) qn[h] = *(const float4*)&sq[h * 32 + off];
                 }
                 const uint32_t x = ODD ? w[c + 1] : __builtin_amdgcn_alignbyte(w[c + 1], w[c], 2);
                 const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
@@ -805,6 +814,7 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
     __shared__ __attribute__((aligned(16))) uint32_t s_kv[NB][2][T * 9];
     __shared__ __attribute__((aligned(16))) float s_x[2 * NB * G * 64];
     __shared__ __attribute__((aligned(16))) float s_c[NB][T * GP];
+    __shared__ __attribute__((aligned(16))) float s_q[NB][G * 32];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -829,10 +839,10 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
     const int abs_split = A.split_off + lsplit;
     if (wave & 1)
         slice_body<D, G, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                            s_kv[wave][1], s_x, s_c[wave]);
+                            s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
     else
         slice_body<D, G, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                            s_kv[wave][1], s_x, s_c[wave]);
+                            s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
 }
 
 // Merge the split partials of one (sequence, query head) in split order.  One
