@@ -212,6 +212,24 @@ def batched(args, torch, kvd, inputs, link):
     return res
 
 
+def tiled(args, torch, kvd, inputs, link):
+    """131072 rows x 64 layers host-resident at a 128 MiB budget, where a
+    whole-layer ring declines: each layer streamed in tiles through a depth-1
+    ring instead (ordered tiles vs pipelined tiles)."""
+    from decode_attention_offloaded_amd import tiled as tl
+    c = inputs.config(3)
+    res = tl.run_tiled(torch, kvd, inputs, c, n_layers=args.tiled_layers, depths=(0, 1), budget_bytes=128 << 20,
+                       tokens=args.tiled_tokens, warmup=1, log=log, distinct_layers=4)
+    res.pop("outs", None)
+    peak = max(link.values())
+    res["link_peak_GBps"] = peak
+    for arm in res["arms"].values():
+        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    log("tiled (%d rows per tile, %d tiles per layer): %s" % (res["tile_rows"], res["tiles_per_layer"], {
+        k: (v["ms_per_token"], v["staged_GBps"]) for k, v in res["arms"].items()}))
+    return res
+
+
 def long_context(args, torch, kvd, inputs):
     """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
     from decode_attention_offloaded_amd import stack
@@ -308,6 +326,9 @@ def main():
     ap.add_argument("--batched", type=int, default=1, help="run the 16-sequence mixed-residency stack")
     ap.add_argument("--batched-layers", type=int, default=64)
     ap.add_argument("--batched-tokens", type=int, default=4)
+    ap.add_argument("--tiled", type=int, default=1, help="run 131072 rows at 128 MiB in ring-streamed tiles")
+    ap.add_argument("--tiled-layers", type=int, default=64)
+    ap.add_argument("--tiled-tokens", type=int, default=3)
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
@@ -346,11 +367,13 @@ def main():
         "device_curve": d["curve"],
         "calibration_copy_bytes": calib,
     }
-    link = link_peak(torch) if (args.pipeline or args.batched) else None
+    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled) else None
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
     if args.batched:
         out["batched"] = batched(args, torch, kvd, inputs, link)
+    if args.tiled:
+        out["tiled"] = tiled(args, torch, kvd, inputs, link)
     if args.long:
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:

@@ -81,7 +81,27 @@ struct LaunchArgs {
     int32_t n_items;
     int32_t split_off;    // absolute index of this launch's first split
     float scale_log2e;
+    // Unnormalised result instead of `out` (tile-streamed attention): o
+    // [seq][n_head_q][D], m and l [seq][n_head_q]; null for a normal call.
+    float* part_o;
+    float* part_m;
+    float* part_l;
 };
+
+// Final result of one (sequence, query head) at dimension i: out = O / L, or
+// the unnormalised (O, M, L) when the call asked for a partial result.
+__device__ inline void write_final(const LaunchArgs& A, int D, size_t sh, int i, float O, float M, float L,
+                                   bool lead) {
+    if (A.part_o) {
+        A.part_o[sh * D + i] = O;
+        if (lead) {
+            A.part_m[sh] = M;
+            A.part_l[sh] = L;
+        }
+    } else {
+        A.out[sh * D + i] = O / L;
+    }
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kRsrcWord3);
@@ -526,7 +546,7 @@ __global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
             O = fmaf(a, ov, O);
         }
         if (single) {
-            A.out[((size_t)s * n_head_q + hq0 + h) * D + i] = O / L;
+            write_final(A, D, (size_t)s * n_head_q + hq0 + h, i, O, M, L, i == 0);
         } else {
             const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
             A.po[pi * D + i] = O;
@@ -787,7 +807,10 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     if (slot == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if (single) {
+            if (single && A.part_o) {
+                *(float4*)&A.part_o[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
+                    make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+            } else if (single) {
                 const float inv = 1.f / l[h];
                 *(float4*)&A.out[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
                     make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
@@ -797,12 +820,18 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             }
         }
     }
-    if (!single && wave == 0 && lane == 0) {
+    if (wave == 0 && lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-            A.pm[pi] = m[h];
-            A.pl[pi] = l[h];
+            if (!single) {
+                const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
+                A.pm[pi] = m[h];
+                A.pl[pi] = l[h];
+            } else if (A.part_o) {
+                const size_t sh = (size_t)s * n_head_q + hq0 + h;
+                A.part_m[sh] = m[h];
+                A.part_l[sh] = l[h];
+            }
         }
     }
 }
@@ -845,43 +874,32 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
                             s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
 }
 
-// Merge the split partials of one (sequence, query head) in split order.  One
-// workgroup per (sequence, query head), one wave per 32 dims; lanes take
-// splits, 64 at a time.  Every lane loads its split's maximum, sum and 32
-// partial outputs together (one round trip), the weights follow from a wave
-// maximum, and the 64 weighted rows are summed column by column through LDS,
-// in split order, so the result does not depend on timing.  A separate
-// launch, so the partials written by the decode kernel are visible without
-// cache maintenance inside a kernel.
-template <int D>
-__global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
-    constexpr int NWV = D / 32;
-    __shared__ float s_o[NWV][64][33];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int hq = blockIdx.x % n_head_q;
-    const int s = blockIdx.x / n_head_q;
-    const SeqDesc& SQ = A.seq[s];
-    const int S = SQ.n_split;
-    if (S <= 1) return;  // written directly by the decode kernel
-    const int first = A.split_off + SQ.split_base;
-    float(*so)[33] = s_o[wave];
-    float M = -INFINITY, L = 0.f, acc = 0.f;  // acc: dimension 32 * wave + lane (lanes < 32)
-    for (int c0 = 0; c0 < S; c0 += 64) {
+// Merge n partial results (m_k, l_k, o_k) of one (sequence, query head) in
+// index order.  One wave per 32 dims; lanes take partials, 64 at a time.
+// Every lane loads its partial's maximum, sum and 32 outputs together (one
+// round trip), the weights follow from a wave maximum, and the 64 weighted
+// rows are summed column by column through LDS in index order, so the result
+// does not depend on timing.  `load(k, m, l, v)` fetches partial k (k < n).
+// Returns, in lanes 0..31, dimension 32 * wave + lane of O = sum e^(m_k - M) o_k,
+// with M and L = sum e^(m_k - M) l_k in every lane.
+template <class Load>
+__device__ inline void merge_rows(const Load& load, int n, int lane, float (*so)[33], float& O, float& M, float& L) {
+    M = -INFINITY;
+    L = 0.f;
+    O = 0.f;
+    for (int c0 = 0; c0 < n; c0 += 64) {
         const int k = c0 + lane;
-        const bool ok = k < S;
-        const size_t pi = (size_t)(first + (ok ? k : c0)) * n_head_q + hq;
-        const float pm = ok ? A.pm[pi] : -INFINITY;
-        const float pl = ok ? A.pl[pi] : 0.f;
-        const float4* po = (const float4*)(A.po + pi * D + 32 * wave);
+        const bool ok = k < n;
+        float pm, pl;
         float4 v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = po[j];
+        load(ok ? k : c0, pm, pl, v);
+        pm = ok ? pm : -INFINITY;
+        pl = ok ? pl : 0.f;
         const float Mn = fmaxf(M, wave_max(pm));
         const float w = ok ? __builtin_amdgcn_exp2f(pm - Mn) : 0.f;
         const float alpha = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
         L = fmaf(L, alpha, wave_sum(w * pl));
-        acc *= alpha;
+        O *= alpha;
         M = Mn;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -895,11 +913,64 @@ __global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs
             float t = 0.f;
 #pragma unroll 16
             for (int r = 0; r < 64; ++r) t += so[r][lane];
-            acc += t;
+            O += t;
         }
         wave_lds_sync();
     }
-    if (lane < 32) A.out[((size_t)s * n_head_q + hq) * D + 32 * wave + lane] = acc / L;
+}
+
+// Merge the split partials of one (sequence, query head): one workgroup per
+// (sequence, query head), one wave per 32 dims.  A separate launch, so the
+// partials written by the decode kernel are visible without cache
+// maintenance inside a kernel.
+template <int D>
+__global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
+    constexpr int NWV = D / 32;
+    __shared__ float s_o[NWV][64][33];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hq = blockIdx.x % n_head_q;
+    const int s = blockIdx.x / n_head_q;
+    const SeqDesc& SQ = A.seq[s];
+    const int S = SQ.n_split;
+    if (S <= 1) return;  // written directly by the decode kernel
+    const int first = A.split_off + SQ.split_base;
+    auto load = [&](int k, float& pm, float& pl, float4 (&v)[8]) {
+        const size_t pi = (size_t)(first + k) * n_head_q + hq;
+        pm = A.pm[pi];
+        pl = A.pl[pi];
+        const float4* po = (const float4*)(A.po + pi * D + 32 * wave);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = po[j];
+    };
+    float O, M, L;
+    merge_rows(load, S, lane, s_o[wave], O, M, L);
+    if (lane < 32) write_final(A, D, (size_t)s * n_head_q + hq, 32 * wave + lane, O, M, L, wave == 0 && lane == 0);
+}
+
+// Merge the partial results of n_part calls over disjoint row sets of the
+// same sequences (tile-streamed attention): partial t holds o [S][H][D], then
+// m [S][H], then l [S][H] (S sequences, H query heads), (D + 2) S H floats.
+template <int D>
+__global__ void __launch_bounds__(64 * (D / 32)) merge_kernel(const float* parts, int32_t n_part, int32_t n_sh,
+                                                               float* out) {
+    constexpr int NWV = D / 32;
+    __shared__ float s_o[NWV][64][33];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const size_t sh = blockIdx.x;  // sequence * H + query head
+    const size_t stride = (size_t)(D + 2) * n_sh;
+    auto load = [&](int k, float& pm, float& pl, float4 (&v)[8]) {
+        const float* p = parts + (size_t)k * stride;
+        pm = p[(size_t)n_sh * D + sh];
+        pl = p[(size_t)n_sh * (D + 1) + sh];
+        const float4* po = (const float4*)(p + sh * D + 32 * wave);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = po[j];
+    };
+    float O, M, L;
+    merge_rows(load, n_part, lane, s_o[wave], O, M, L);
+    if (lane < 32) out[sh * D + 32 * wave + lane] = O / L;
 }
 
 typedef void (*decode_fn)(const LaunchArgs);
@@ -959,11 +1030,18 @@ extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* byt
     return KVD_OK;
 }
 
-extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
-    clear_error();
+namespace kvd {
+namespace {
+
+// Shared by the normal and the partial-result entry points: `part` null ->
+// write out; else write (o, m, l) at part (layout of merge_kernel's input).
+int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
     AttendPlan p;
     int rc = plan_attend(a, &p);
     if (rc != KVD_OK) return rc;
+    if (!part && !a->out) return fail(KVD_EINVAL, "out must not be NULL");
+    if (!part && (uintptr_t)a->out % 16) return fail(KVD_EINVAL, "out must be 16-byte aligned");
+    if (part && (uintptr_t)part % 16) return fail(KVD_EINVAL, "partial must be 16-byte aligned");
     if (p.ws_bytes > 0) {
         if (!a->workspace || a->workspace_bytes < p.ws_bytes)
             return fail(KVD_EINVAL, "workspace of %zu bytes needed, %zu given", p.ws_bytes,
@@ -1007,7 +1085,14 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
             nsplit += sp.n_split;
         }
         L.q = a->q + (size_t)s0 * n_head_q * D;
-        L.out = a->out + (size_t)s0 * n_head_q * D;
+        const size_t n_sh = (size_t)a->n_seq * n_head_q;
+        if (part) {
+            L.part_o = part + (size_t)s0 * n_head_q * D;
+            L.part_m = part + n_sh * D + (size_t)s0 * n_head_q;
+            L.part_l = part + n_sh * (D + 1) + (size_t)s0 * n_head_q;
+        } else {
+            L.out = a->out + (size_t)s0 * n_head_q * D;
+        }
         if (p.ws_bytes > 0) {
             L.pm = (float*)(ws + p.off_pm);
             L.pl = (float*)(ws + p.off_pl);
@@ -1032,5 +1117,42 @@ extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
             if (e != hipSuccess) return fail(KVD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
         }
     }
+    return KVD_OK;
+}
+
+}  // namespace
+}  // namespace kvd
+
+extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
+    clear_error();
+    return launch_attend(a, stream, nullptr);
+}
+
+extern "C" int kvd_attend_decode_partial(const kvd_attn_args* a, float* partial, void* stream) {
+    clear_error();
+    if (!partial) return fail(KVD_EINVAL, "partial must not be NULL");
+    return launch_attend(a, stream, partial);
+}
+
+extern "C" int kvd_attend_merge(const float* partials, int32_t n_part, int32_t n_seq, int32_t n_head_q,
+                                int32_t head_dim, float* out, void* stream) {
+    clear_error();
+    if (!partials || !out) return fail(KVD_EINVAL, "partials and out must not be NULL");
+    if (n_part < 1 || n_part > (1 << 20)) return fail(KVD_EINVAL, "n_part %d out of range [1, 2^20]", n_part);
+    if (n_seq < 1 || n_head_q < 1 || (int64_t)n_seq * n_head_q > (1 << 24))
+        return fail(KVD_EINVAL, "n_seq %d x n_head_q %d out of range", n_seq, n_head_q);
+    if (head_dim != 64 && head_dim != 128) return fail(KVD_EINVAL, "head_dim %d must be 64 or 128", head_dim);
+    if ((uintptr_t)partials % 16 || (uintptr_t)out % 16)
+        return fail(KVD_EINVAL, "partials and out must be 16-byte aligned");
+    const int32_t n_sh = n_seq * n_head_q;
+    if (n_sh % 2) return fail(KVD_EINVAL, "n_seq x n_head_q must be even (partials stay 16-byte aligned)");
+    if (head_dim == 128)
+        hipLaunchKernelGGL(merge_kernel<128>, dim3((unsigned)n_sh), dim3(256), 0, (hipStream_t)stream, partials,
+                           n_part, n_sh, out);
+    else
+        hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)n_sh), dim3(128), 0, (hipStream_t)stream, partials,
+                           n_part, n_sh, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(KVD_EHIP, "merge kernel launch: %s", hipGetErrorString(e));
     return KVD_OK;
 }

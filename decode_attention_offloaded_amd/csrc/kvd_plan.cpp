@@ -30,8 +30,8 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     if (a->split_rows < 0 || a->split_rows % kSubRows != 0 || a->split_rows > (1 << 24))
         return fail(KVD_EINVAL, "split_rows %d must be 0 or a positive multiple of 64", a->split_rows);
     if (!isfinite(a->scale)) return fail(KVD_EINVAL, "scale is not finite");
-    if (!a->q || !a->out || !a->segs) return fail(KVD_EINVAL, "q, out and segs must not be NULL");
-    if ((uintptr_t)a->q % 4 || (uintptr_t)a->out % 4) return fail(KVD_EINVAL, "q/out must be 4-byte aligned");
+    if (!a->q || !a->segs) return fail(KVD_EINVAL, "q and segs must not be NULL");
+    if ((uintptr_t)a->q % 16) return fail(KVD_EINVAL, "q must be 16-byte aligned");
 
     const int D = a->head_dim;
     const int chunk = D / 32 * 34;

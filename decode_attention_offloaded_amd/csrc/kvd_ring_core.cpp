@@ -316,6 +316,30 @@ extern "C" int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, siz
     return KVD_OK;
 }
 
+extern "C" int kvd_ring_tile_rows(int32_t depth, size_t budget_bytes, int64_t row_bytes, double max_tile_bytes,
+                                  int64_t* tile_rows) {
+    clear_error();
+    if (!tile_rows) return fail(KVD_EINVAL, "tile_rows is NULL");
+    *tile_rows = 0;
+    if (depth < 1) return fail(KVD_EINVAL, "depth %d < 1: tiles are staged through a ring", depth);
+    if (row_bytes <= 0 || row_bytes > (1 << 24)) return fail(KVD_EINVAL, "row_bytes %lld out of range", (long long)row_bytes);
+    if (!(max_tile_bytes >= 0.0)) return fail(KVD_EINVAL, "max_tile_bytes must be >= 0");
+    const int64_t budget = budget_bytes > (size_t)INT64_MAX ? INT64_MAX : (int64_t)budget_bytes;
+    // largest multiple of 64 rows whose ring fits the budget (inclusive)
+    int64_t rows = budget / ((int64_t)(depth + 2) * 2 * row_bytes);
+    if (max_tile_bytes > 0.0) {
+        const double cap = max_tile_bytes / (2.0 * (double)row_bytes);
+        if (cap < (double)rows) rows = (int64_t)cap;
+    }
+    rows = rows / 64 * 64;
+    if (rows > ((int64_t)1 << 30)) rows = (int64_t)1 << 30;
+    int64_t need = 0;
+    while (rows > 0 && (!ring_need_bytes(depth, rows, row_bytes, &need) || need > budget)) rows -= 64;
+    if (rows < 64) return KVD_DECLINED;
+    *tile_rows = rows;
+    return KVD_OK;
+}
+
 extern "C" void kvd_ring_destroy(kvd_ring* ring) {
     clear_error();
     delete ring;

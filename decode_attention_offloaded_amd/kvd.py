@@ -78,6 +78,14 @@ def _declare(L):
     L.kvd_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(c_size_t)]
     L.kvd_attend_decode.restype = c_int
     L.kvd_attend_decode.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
+    L.kvd_attend_decode_partial.restype = c_int
+    L.kvd_attend_decode_partial.argtypes = [ctypes.POINTER(AttnArgs), c_void_p, c_void_p]
+    L.kvd_attend_merge.restype = c_int
+    L.kvd_attend_merge.argtypes = [c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   c_void_p, c_void_p]
+    L.kvd_ring_tile_rows.restype = c_int
+    L.kvd_ring_tile_rows.argtypes = [ctypes.c_int32, c_size_t, ctypes.c_int64, ctypes.c_double,
+                                     ctypes.POINTER(ctypes.c_int64)]
     L.kvd_ring_create.restype = c_void_p
     L.kvd_ring_create.argtypes = [ctypes.c_int32, c_size_t]
     L.kvd_ring_stage_layer.restype = c_int
@@ -215,6 +223,63 @@ def attend_decode(q, out, segs, n_head_kv: int, window: int = 0, scale: Optional
         a.workspace_bytes = ws.numel()
     _check(lib().kvd_attend_decode(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out
+
+
+def partial_floats(n_seq: int, n_head_q: int, head_dim: int) -> int:
+    """Floats of one partial result: o [S][H][D], then m [S][H], then l [S][H]."""
+    return (head_dim + 2) * n_seq * n_head_q
+
+
+def attend_decode_partial(q, partial, segs, n_head_kv: int, window: int = 0, scale: Optional[float] = None,
+                          q_pos=None, split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None):
+    """Enqueue decode attention over these rows only, leaving the unnormalised
+    result (o, m, l) in ``partial`` (a float32 CUDA tensor of at least
+    partial_floats(...) elements, e.g. one row of a [n_part, ...] tensor)."""
+    import torch
+    if not (q.is_cuda and partial.is_cuda) or q.dtype != torch.float32 or partial.dtype != torch.float32:
+        raise ValueError("q and partial must be float32 CUDA tensors")
+    if not (q.is_contiguous() and partial.is_contiguous()):
+        raise ValueError("q and partial must be contiguous")
+    n_seq, n_head_q, head_dim = q.shape
+    if partial.numel() < partial_floats(n_seq, n_head_q, head_dim):
+        raise ValueError("partial is too small")
+    a, keep = make_args(q, q, segs, n_head_kv, window, scale, q_pos, split_rows)
+    a.out = None
+    nbytes = workspace_bytes(a)
+    ws = (workspace or _default_ws).get(nbytes, q.device)
+    if ws is not None:
+        a.workspace = ws.data_ptr()
+        a.workspace_bytes = ws.numel()
+    _check(lib().kvd_attend_decode_partial(ctypes.byref(a), ctypes.c_void_p(partial.data_ptr()),
+                                           ctypes.c_void_p(_stream_handle(stream))))
+    return partial
+
+
+def attend_merge(partials, n_part: int, out, stream=None):
+    """out[S, H, D] = merge of partials[0:n_part] (a contiguous float32 CUDA
+    tensor holding n_part partial results back to back), in part order."""
+    import torch
+    if not (partials.is_cuda and out.is_cuda) or partials.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("partials and out must be float32 CUDA tensors")
+    if not (partials.is_contiguous() and out.is_contiguous()):
+        raise ValueError("partials and out must be contiguous")
+    n_seq, n_head_q, head_dim = out.shape
+    if partials.numel() < n_part * partial_floats(n_seq, n_head_q, head_dim):
+        raise ValueError("partials holds fewer than n_part results")
+    _check(lib().kvd_attend_merge(ctypes.c_void_p(partials.data_ptr()), int(n_part), int(n_seq), int(n_head_q),
+                                  int(head_dim), ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(_stream_handle(stream))))
+    return out
+
+
+def tile_rows(depth: int, budget_bytes: int, row_bytes: int, max_tile_bytes: float = 0.0):
+    """(rc, rows) from kvd_ring_tile_rows: rc is KVD_OK or KVD_DECLINED."""
+    r = ctypes.c_int64(0)
+    rc = lib().kvd_ring_tile_rows(int(depth), int(budget_bytes), int(row_bytes), float(max_tile_bytes),
+                                  ctypes.byref(r))
+    if rc < 0:
+        raise KvdError(rc, last_error())
+    return rc, int(r.value)
 
 
 # ------------------------------------------------------------------ staging ring

@@ -113,8 +113,9 @@ typedef struct kvd_attn_args {
     int32_t split_rows;  /* 0 = plan from shape; else rows per split, a
                             multiple of 64 (testing and tuning) */
     float scale;         /* softmax scale, usually 1/sqrt(head_dim); finite */
-    const float* q;      /* device fp32 [n_seq][n_head_q][head_dim] */
-    float* out;          /* device fp32 [n_seq][n_head_q][head_dim] */
+    const float* q;      /* device fp32 [n_seq][n_head_q][head_dim], 16-byte aligned */
+    float* out;          /* device fp32 [n_seq][n_head_q][head_dim], 16-byte aligned
+                            (unused, may be NULL, for kvd_attend_decode_partial) */
     const kvd_kv_seg* segs;  /* HOST array [n_seq][n_seg]; read during the call only */
     const int64_t* q_pos;    /* HOST array [n_seq] of query positions, or NULL =
                                 the position of the last row of the last segment */
@@ -134,6 +135,33 @@ int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
  * KVD_EINVAL (bad shapes, unaligned or null pointers, a sequence with no
  * visible row, workspace too small) or KVD_EHIP (launch failure). */
 int kvd_attend_decode(const kvd_attn_args* args, void* stream);
+
+/* Tile-streamed attention ("F5 — Advanced KV Cache Techniques", F5-opt W4,
+ * M7 Rolling KV: a slot pool, a tile loop and an inter-tile online-softmax
+ * merge of the per-tile results).  A layer's rows are attended in tiles, one
+ * call per tile over that tile's rows only, each leaving an unnormalised
+ * result; one merge then gives the attention over the union of the tiles.
+ *
+ * kvd_attend_decode_partial: as kvd_attend_decode (same arguments, same
+ * validation, same workspace), but instead of `out` it writes to `partial`
+ * (device, 16-byte aligned, (head_dim + 2) * n_seq * n_head_q floats):
+ *   o [n_seq][n_head_q][head_dim] = sum_t e^(x_t - m) V[t]
+ *   m [n_seq][n_head_q]           = the reference maximum, in units of
+ *                                    x_t = scale * log2(e) * q . K[t]
+ *   l [n_seq][n_head_q]           = sum_t e^(x_t - m)   (e^ taken base 2)
+ * over the rows visible in this call.  Every sequence needs at least one
+ * visible row in every call.  `args->out` is not used. */
+int kvd_attend_decode_partial(const kvd_attn_args* args, float* partial, void* stream);
+
+/* Merge n_part partial results, laid out back to back (partial t at
+ * partials + t * (head_dim + 2) * n_seq * n_head_q), into
+ * out[n_seq][n_head_q][head_dim] = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t
+ * with M = max_t m_t, merged in t order (the result does not depend on timing).
+ * Device pointers, 16-byte aligned; head_dim 64 or 128; 1 <= n_part <= 2^20;
+ * n_seq * n_head_q even (so every partial starts on a 16-byte boundary).
+ * Asynchronous on `stream`.  Returns KVD_OK, KVD_EINVAL or KVD_EHIP. */
+int kvd_attend_merge(const float* partials, int32_t n_part, int32_t n_seq, int32_t n_head_q, int32_t head_dim,
+                     float* out, void* stream);
 
 /* ==================================================================== staging ring
  * A ring stages one attention layer's K and V from pinned host memory into
@@ -245,6 +273,20 @@ int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, size_t out_siz
 /* Wait for the transfer stream and every slot's release, then free slots,
  * events and the transfer stream.  NULL is a no-op. */
 void kvd_ring_destroy(kvd_ring* ring);
+
+/* Tile size for tile-streamed attention through a ring of this depth and
+ * budget ("F5 — Advanced KV Cache Techniques", F5-opt: tiles of a spilled
+ * layer streamed through a slot pool; tile bytes bounded by
+ * compute_ms * effective_bw * 0.8).  Sets *tile_rows to the largest multiple
+ * of 64 rows such that the ring, (depth + 2) * 2 * tile_rows * row_bytes
+ * bytes, fits budget_bytes (inclusive) and, when max_tile_bytes > 0, one
+ * tile's K + V, 2 * tile_rows * row_bytes, is at most max_tile_bytes (the
+ * caller passes compute_ms * effective_bw * 0.8, or 0 for no such bound).
+ * Returns KVD_OK, KVD_DECLINED (*tile_rows = 0: not even 64 rows fit) or
+ * KVD_EINVAL (depth < 1, row_bytes out of (0, 2^24], max_tile_bytes < 0 or
+ * NaN, tile_rows NULL).  Host-only; allocates nothing. */
+int kvd_ring_tile_rows(int32_t depth, size_t budget_bytes, int64_t row_bytes, double max_tile_bytes,
+                       int64_t* tile_rows);
 
 #ifdef __cplusplus
 }

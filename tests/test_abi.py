@@ -118,3 +118,40 @@ def test_ring_create_and_stats_without_device_work():
         r.stage(0, kvd.STAGE_PREFETCH, 0x1000, 0x2000, 1088, 10, 11, 10, stream=0)  # stable > n_rows
     r.close()
     L.kvd_ring_destroy(None)
+
+
+def test_tile_rows_is_the_largest_fitting_multiple_of_64(oracle):
+    """kvd_ring_tile_rows against a brute-force search with the oracle's ring sizing."""
+    rb = 1088
+    for depth in (1, 2, 3):
+        for budget in (0, 1 << 20, 64 << 20, 128 << 20, 134_111_232, 134_111_231, 1 << 30):
+            rc, rows = kvd.tile_rows(depth, budget, rb)
+            best = 0
+            r = 64
+            while oracle.ring_fits(depth, r, rb, budget):
+                best = r
+                r += 64
+            if best == 0:
+                assert rc == kvd.KVD_DECLINED and rows == 0, (depth, budget)
+            else:
+                assert rc == kvd.KVD_OK and rows == best, (depth, budget, rows, best)
+    # 128 MiB at depth 1: 20544 rows (3 slots x 2 x 20544 x 1088 = 134,111,232 B)
+    assert kvd.tile_rows(1, 128 << 20, rb) == (kvd.KVD_OK, 20544)
+    # the compute-window bound: one tile's K+V at most max_tile_bytes
+    rc, rows = kvd.tile_rows(1, 1 << 30, rb, max_tile_bytes=2.7e6)
+    assert rc == kvd.KVD_OK and rows == int(2.7e6 / (2 * rb)) // 64 * 64
+    for bad in ((0, 1 << 20, rb, 0.0), (1, 1 << 20, 0, 0.0), (1, 1 << 20, rb, -1.0), (1, 1 << 20, rb, float("nan"))):
+        with pytest.raises(kvd.KvdError):
+            kvd.tile_rows(*bad)
+
+
+def test_merge_and_partial_validate_before_launch():
+    L = kvd.lib()
+    assert L.kvd_attend_merge(None, 1, 1, 8, 128, ctypes.c_void_p(0x1000), None) == kvd.KVD_EINVAL
+    assert L.kvd_attend_merge(ctypes.c_void_p(0x1000), 0, 1, 8, 128, ctypes.c_void_p(0x2000), None) == kvd.KVD_EINVAL
+    assert L.kvd_attend_merge(ctypes.c_void_p(0x1000), 2, 1, 8, 96, ctypes.c_void_p(0x2000), None) == kvd.KVD_EINVAL
+    assert L.kvd_attend_merge(ctypes.c_void_p(0x1008), 2, 1, 8, 128, ctypes.c_void_p(0x2000), None) == kvd.KVD_EINVAL
+    assert L.kvd_attend_merge(ctypes.c_void_p(0x1000), 2, 1, 7, 128, ctypes.c_void_p(0x2000), None) == kvd.KVD_EINVAL
+    a, _ = _args()
+    assert L.kvd_attend_decode_partial(ctypes.byref(a), None, None) == kvd.KVD_EINVAL
+    assert L.kvd_attend_decode_partial(ctypes.byref(a), ctypes.c_void_p(0x1004), None) == kvd.KVD_EINVAL
