@@ -230,6 +230,68 @@ def tiled(args, torch, kvd, inputs, link):
     return res
 
 
+def layer_compute_ms(torch, kvd, inputs, n_rows, reps=10):
+    """Per-layer compute of the host-resident stack: the bf16 GEMV stand-in plus
+    attention over n_rows device-resident rows (the planner's compute_ms)."""
+    c = inputs.config(3)
+    dev = torch.device("cuda:0")
+    m, n = c.extra.get("gemv", (5120, 27648))
+    w = torch.randn(m, n, dtype=torch.bfloat16, device=dev) * 0.02
+    x = torch.randn(1, m, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(1, n, dtype=torch.bfloat16, device=dev)
+    r = np.random.default_rng([c.seed, 555])
+    k = torch.from_numpy(inputs.random_kv_rows(r, n_rows, c.n_head_kv, c.head_dim)).to(dev)
+    v = torch.from_numpy(inputs.random_kv_rows(r, n_rows, c.n_head_kv, c.head_dim)).to(dev)
+    q = torch.from_numpy(inputs.random_q(r, 1, c.n_head_q, c.head_dim)).to(dev)
+    out = torch.empty_like(q)
+    for _ in range(2):
+        torch.matmul(x, w, out=y)
+        kvd.attend_decode(q, out, [[(k, v, 0)]], c.n_head_kv)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, w, out=y)
+        kvd.attend_decode(q, out, [[(k, v, 0)]], c.n_head_kv)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def residency(args, torch, kvd, inputs, link):
+    """131072 rows x 64 layers: what a device-memory budget buys -- the
+    residency planner's choice against the other option, measured."""
+    from decode_attention_offloaded_amd import stack
+    c = inputs.config(3)
+    L, n = args.residency_layers, c.n_ctx
+    lb = 2 * n * c.row_bytes
+    peak = max(link.values())
+    cms = layer_compute_ms(torch, kvd, inputs, n)
+    arms, plans = [], {}
+    for gib in (1, 4):
+        budget = gib << 30
+        plan = kvd.plan_residency(L, lb, budget, 1, peak, cms)
+        ring_k = max(0, min(L - 1, (budget - 3 * lb) // lb)) if budget >= 3 * lb else None
+        ord_k = min(L, budget // lb)
+        plans[str(gib)] = plan
+        if ring_k is not None:
+            arms.append(("%dGiB_ring+%d" % (gib, ring_k), 1, budget, ring_k))
+        arms.append(("%dGiB_ordered+%d" % (gib, ord_k), 0, 0, ord_k))
+    res = stack.run_residency(torch, kvd, inputs, c, arms, n_layers=L, tokens=args.residency_tokens, warmup=1,
+                              log=log, distinct_layers=4)
+    res["compute_ms_per_layer"] = round(cms, 4)
+    res["link_peak_GBps"] = peak
+    res["plans"] = plans
+    for gib, plan in plans.items():
+        pick = "%sGiB_%s+%d" % (gib, "ring" if plan["use_ring"] else "ordered", plan["n_resident"])
+        plan["picked_arm"] = pick
+        plan["picked_is_fastest"] = bool(min((v["ms_per_token"], k) for k, v in res["arms"].items()
+                                             if k.startswith(gib + "GiB"))[1] == pick)
+    log("residency: %s; plans %s" % ({k: v["ms_per_token"] for k, v in res["arms"].items()},
+                                     {k: v["picked_arm"] for k, v in plans.items()}))
+    return res
+
+
 def long_context(args, torch, kvd, inputs):
     """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
     from decode_attention_offloaded_amd import stack
@@ -329,6 +391,9 @@ def main():
     ap.add_argument("--tiled", type=int, default=1, help="run 131072 rows at 128 MiB in ring-streamed tiles")
     ap.add_argument("--tiled-layers", type=int, default=64)
     ap.add_argument("--tiled-tokens", type=int, default=3)
+    ap.add_argument("--residency", type=int, default=1, help="run the 131072-row residency-planner arms")
+    ap.add_argument("--residency-layers", type=int, default=64)
+    ap.add_argument("--residency-tokens", type=int, default=3)
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
@@ -367,13 +432,15 @@ def main():
         "device_curve": d["curve"],
         "calibration_copy_bytes": calib,
     }
-    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled) else None
+    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency) else None
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
     if args.batched:
         out["batched"] = batched(args, torch, kvd, inputs, link)
     if args.tiled:
         out["tiled"] = tiled(args, torch, kvd, inputs, link)
+    if args.residency:
+        out["residency"] = residency(args, torch, kvd, inputs, link)
     if args.long:
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:

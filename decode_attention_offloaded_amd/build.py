@@ -22,7 +22,7 @@ CODE_OBJECT = ["-mcode-object-version=5"]  # loadable by the ROCm 7.0 runtime to
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HIP_SOURCES = ["kvd_attend.hip"]
-HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp"]
+HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp"]
 
 
 def _compile(src: str) -> str:

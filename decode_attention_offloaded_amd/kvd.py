@@ -49,6 +49,12 @@ class SlotView(ctypes.Structure):
                 ("row_stride", ctypes.c_int64), ("pipelined", ctypes.c_int32), ("slot", ctypes.c_int32)]
 
 
+class ResidencyPlan(ctypes.Structure):
+    _fields_ = [("n_resident", ctypes.c_int32), ("use_ring", ctypes.c_int32), ("resident_bytes", ctypes.c_int64),
+                ("ring_bytes", ctypes.c_int64), ("staged_bytes_per_step", ctypes.c_int64),
+                ("est_ms_per_step", ctypes.c_double)]
+
+
 class RingStats(ctypes.Structure):
     _fields_ = [("depth", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("engaged", ctypes.c_int32),
                 ("declined", ctypes.c_int32), ("device", ctypes.c_int32), ("reserved", ctypes.c_int32),
@@ -86,6 +92,9 @@ def _declare(L):
     L.kvd_ring_tile_rows.restype = c_int
     L.kvd_ring_tile_rows.argtypes = [ctypes.c_int32, c_size_t, ctypes.c_int64, ctypes.c_double,
                                      ctypes.POINTER(ctypes.c_int64)]
+    L.kvd_plan_residency.restype = c_int
+    L.kvd_plan_residency.argtypes = [ctypes.c_int32, ctypes.c_int64, c_size_t, ctypes.c_int32, ctypes.c_double,
+                                     ctypes.c_double, ctypes.POINTER(ResidencyPlan)]
     L.kvd_ring_create.restype = c_void_p
     L.kvd_ring_create.argtypes = [ctypes.c_int32, c_size_t]
     L.kvd_ring_stage_layer.restype = c_int
@@ -280,6 +289,15 @@ def tile_rows(depth: int, budget_bytes: int, row_bytes: int, max_tile_bytes: flo
     if rc < 0:
         raise KvdError(rc, last_error())
     return rc, int(r.value)
+
+
+def plan_residency(n_layers: int, layer_bytes: int, budget_bytes: int, depth: int, link_gbps: float = 0.0,
+                   compute_ms: float = 0.0) -> dict:
+    """kvd_plan_residency as a dict."""
+    p = ResidencyPlan()
+    _check(lib().kvd_plan_residency(int(n_layers), int(layer_bytes), int(budget_bytes), int(depth),
+                                    float(link_gbps), float(compute_ms), ctypes.byref(p)))
+    return {name: getattr(p, name) for name, _ in ResidencyPlan._fields_}
 
 
 # ------------------------------------------------------------------ staging ring

@@ -104,10 +104,18 @@ class Stack:
     """Drives one arm (a ring of some depth and budget) over a HostKV."""
 
     def __init__(self, torch, kvd, cfg, host: HostKV, n_rows: int, depth: int, budget_bytes: int,
-                 gemv_weights=None, stream=None, new_rows=None):
+                 gemv_weights=None, stream=None, new_rows=None, resident: int = 0):
         self.torch, self.kvd, self.cfg, self.host = torch, kvd, cfg, host
         self.n_rows, self.depth = n_rows, depth
         dev = torch.device("cuda:0")
+        # layers [0, resident) keep their K/V on the device (a resident
+        # prefix); the rest are staged through the ring each step
+        self.resident = max(0, min(int(resident), host.n_layers))
+        self.dev_k = [torch.from_numpy(host.k_rows(l)[:n_rows]).to(dev) for l in range(self.resident)]
+        self.dev_v = [torch.from_numpy(host.v_rows(l)[:n_rows]).to(dev) for l in range(self.resident)]
+        self.pool_dev = None
+        if self.resident and new_rows is not None and hasattr(new_rows, "rows"):
+            self.pool_dev = [(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev)) for k, v in new_rows.rows]
         self.stream = stream or torch.cuda.Stream(device=dev)
         self.ring = kvd.Ring(depth, budget_bytes)
         rb = host.row_bytes
@@ -137,9 +145,10 @@ class Stack:
         torch, kvd, h = self.torch, self.kvd, self.host
         L, N, s = h.n_layers, self.depth, self.stream
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        R = self.resident
         with torch.cuda.stream(s):
             e0.record(s)
-            for l in range(min(N, L)):
+            for l in range(R, min(R + N, L)):
                 self._stage(l, kvd.STAGE_PREFETCH)
             for l in range(L):
                 if self.gemv is not None:
@@ -148,6 +157,18 @@ class Stack:
                     kr, vr = self.new_rows(t, l)
                     h.k_rows(l)[self.n_rows - 1] = kr
                     h.v_rows(l)[self.n_rows - 1] = vr
+                if l < R:
+                    # resident layer: the newest row is written on the device
+                    if self.new_rows is not None:
+                        if self.pool_dev is not None:
+                            kd, vd = self.pool_dev[self.new_rows.index(t, l)]
+                        else:
+                            kd, vd = torch.from_numpy(kr).to(s.device), torch.from_numpy(vr).to(s.device)
+                        self.dev_k[l][self.n_rows - 1].copy_(kd)
+                        self.dev_v[l][self.n_rows - 1].copy_(vd)
+                    kvd.attend_decode(self.q[l], self.out[l], [[(self.dev_k[l], self.dev_v[l], 0)]],
+                                      self.cfg.n_head_kv, workspace=self.ws, stream=s)
+                    continue
                 rc, view = self._stage(l, kvd.STAGE_ACQUIRE)
                 if self.on_view is not None:
                     self.on_view(l, view)
@@ -156,7 +177,7 @@ class Stack:
                 if self.after_attend is not None:
                     self.after_attend(l, view)
                 self.ring.release(l, stream=s)
-                if l + N < L and N > 0:
+                if l + N < L and N > 0 and l + N >= R + N:
                     self._stage(l + N, kvd.STAGE_PREFETCH)
             e1.record(s)
         s.synchronize()
@@ -180,8 +201,12 @@ def token_rows(cfg, pool: int = 4):
     rows = [(inputs.random_kv_rows(g, 1, cfg.n_head_kv, cfg.head_dim)[0],
              inputs.random_kv_rows(g, 1, cfg.n_head_kv, cfg.head_dim)[0]) for _ in range(pool * 7)]
 
+    def index(t, l):
+        return (t * 7 + l) % len(rows)
+
     def f(t, l):
-        return rows[(t * 7 + l) % len(rows)]
+        return rows[index(t, l)]
+    f.rows, f.index = rows, index
     return f
 
 
@@ -243,6 +268,66 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
                                "n_acquire_ordered": s["n_acquire_ordered"], "bytes_early": s["bytes_early"],
                                "bytes_late": s["bytes_late"]}
     host.free()
+    del weights
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_residency(torch, kvd, inputs, cfg, arms, n_layers=64, tokens=3, warmup=1, log=print, n_rows=None,
+                  distinct_layers=None, host=None):
+    """Per-token time of several residency arms over one host stack, A/B/B/A.
+
+    arms: list of (name, depth, budget_bytes, resident).  Each arm keeps layers
+    [0, resident) on the device and stages the rest (ring of `depth` within
+    `budget_bytes`, or ordered).  Outputs of every arm must agree bit for bit:
+    attention reads the same bytes whichever memory holds them."""
+    n_rows = n_rows or cfg.n_ctx
+    dev = torch.device("cuda:0")
+    own = host is None
+    if own:
+        t0 = time.perf_counter()
+        host = HostKV(n_layers, n_rows, cfg.row_bytes)
+        host.fill(inputs, cfg, n_rows, distinct=distinct_layers)
+        log("host KV: %d layers x %d rows, %.2f GB pinned, filled in %.1f s" %
+            (n_layers, n_rows, 2 * host.k.nbytes / 1e9, time.perf_counter() - t0))
+    gen = torch.Generator(device=dev).manual_seed(cfg.seed)
+    m, n = cfg.extra.get("gemv", (5120, 27648))
+    weights = [(torch.randn(m, n, dtype=torch.bfloat16, device=dev, generator=gen) * 0.02) for _ in range(n_layers)]
+    rows_fn = token_rows(cfg)
+    compute = torch.cuda.Stream(device=dev)
+    order = list(range(len(arms))) + list(reversed(range(len(arms))))
+    times = {i: [] for i in range(len(arms))}
+    outs, stats = {}, {}
+    for i in order:
+        name, depth, budget, resident = arms[i]
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        st = Stack(torch, kvd, cfg, host, n_rows, depth, budget, gemv_weights=weights, new_rows=rows_fn,
+                   stream=compute, resident=resident)
+        for t in range(warmup):
+            st.token(t)
+        for t in range(warmup, warmup + tokens):
+            times[i].append(st.token(t))
+        outs[i] = [o.clone() for o in st.out]
+        stats[i] = st.ring.stats()
+        st.close()
+        del st
+        torch.cuda.empty_cache()
+    identical = all(torch.equal(a, b) for j in range(1, len(arms)) for a, b in zip(outs[0], outs[j]))
+    res = {"n_ctx": n_rows, "n_layers": n_layers, "tokens_timed": tokens, "bit_identical": bool(identical),
+           "arms": {}}
+    for i, (name, depth, budget, resident) in enumerate(arms):
+        ms = float(np.median(times[i]))
+        s = stats[i]
+        staged = 2 * (n_layers - resident) * n_rows * cfg.row_bytes
+        res["arms"][name] = {"depth": depth, "budget_bytes": budget, "resident_layers": resident,
+                             "ms_per_token": round(ms, 3), "staged_bytes_per_token": staged,
+                             "staged_GBps": round(staged / (ms * 1e-3) / 1e9, 2),
+                             "ring_engaged_bytes": s["ring_bytes"] if s["engaged"] else 0,
+                             "declined": s["declined"], "n_acquire_pipelined": s["n_acquire_pipelined"],
+                             "n_acquire_ordered": s["n_acquire_ordered"]}
+    if own:
+        host.free()
     del weights
     torch.cuda.empty_cache()
     return res

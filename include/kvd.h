@@ -288,6 +288,42 @@ void kvd_ring_destroy(kvd_ring* ring);
 int kvd_ring_tile_rows(int32_t depth, size_t budget_bytes, int64_t row_bytes, double max_tile_bytes,
                        int64_t* tile_rows);
 
+/* ==================================================================== residency
+ * Which layers keep their K/V on the device ("sched: pipeline the delivery
+ * of a host-resident KV cache (R4)", Known limitations: device-resident
+ * layers can remove more host-to-device traffic than a ring of the same bytes
+ * hides; "F5 — Advanced KV Cache Techniques", F5-opt W4: device-resident
+ * whenever the KV fits the budget, spill only under pressure).
+ *
+ * Layers [0, n_resident) stay on the device (a resident prefix: while it is
+ * computed the first staged layer's delivery is in flight); the others are
+ * staged per step, through a depth-`depth` ring of whole layers when use_ring,
+ * else on the ordered path.  The budget covers the resident layers plus the
+ * ring ((depth + 2) * layer_bytes).
+ *
+ * Choice: every layer resident if all fit.  Otherwise, with link_gbps > 0 a
+ * step-time estimate decides between "ring + as many resident layers as fit
+ * beside it" and "no ring + as many resident layers as fit": staged bytes
+ * cross the link at link_gbps; compute is n_layers * compute_ms; ordered =
+ * transfer + compute; ring = max(transfer, compute) + the part of the first
+ * staged layer's delivery that the resident prefix does not cover.  With
+ * link_gbps == 0 the ring is kept whenever it fits.  Host-only; allocates
+ * nothing. */
+typedef struct kvd_residency_plan {
+    int32_t n_resident;            /* layers [0, n_resident) device-resident */
+    int32_t use_ring;              /* 1: stage the rest through the ring; 0: ordered */
+    int64_t resident_bytes;        /* n_resident * layer_bytes */
+    int64_t ring_bytes;            /* (depth + 2) * layer_bytes when use_ring, else 0 */
+    int64_t staged_bytes_per_step; /* (n_layers - n_resident) * layer_bytes */
+    double est_ms_per_step;        /* the estimate the choice used (0 without a model) */
+} kvd_residency_plan;
+
+/* n_layers in [1, 2^20]; layer_bytes = K + V bytes of one layer (all layers
+ * alike), in [1, 2^50]; depth >= 0 (0: no ring); link_gbps and compute_ms
+ * finite and >= 0.  Returns KVD_OK or KVD_EINVAL. */
+int kvd_plan_residency(int32_t n_layers, int64_t layer_bytes, size_t budget_bytes, int32_t depth, double link_gbps,
+                       double compute_ms, kvd_residency_plan* out);
+
 #ifdef __cplusplus
 }
 #endif
