@@ -54,6 +54,42 @@ def random_kv_rows(rng: np.random.Generator, n_rows: int, n_head_kv: int, head_d
     return pack_q8_0(codes, scales.view(np.uint16))
 
 
+Q4_BLOCK_BYTES = 18
+
+
+def row_bytes_q4_0(n_head_kv: int, head_dim: int) -> int:
+    """Bytes of one token row of a q4_0 tensor: every KV head, head_dim/32 blocks of 18 B."""
+    return n_head_kv * (head_dim // QK) * Q4_BLOCK_BYTES
+
+
+def pack_q4_0(nibbles: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Lay out 4-bit codes uint8 [..., n_blocks, 32] (0..15, code j of the block)
+    and binary16 bit patterns [..., n_blocks] as 18-byte q4_0 blocks: byte 2 + j
+    holds code j in its low nibble and code 16 + j in its high nibble."""
+    nib = np.asarray(nibbles, dtype=np.uint8)
+    if (nib > 15).any():
+        raise ValueError("4-bit codes must be 0..15")
+    scale_bits = np.asarray(scale_bits, dtype=np.uint16)
+    lead = nib.shape[:-2]
+    nb = nib.shape[-2]
+    out = np.empty(lead + (nb, Q4_BLOCK_BYTES), dtype=np.uint8)
+    out[..., 0] = (scale_bits & 0xFF).astype(np.uint8)
+    out[..., 1] = (scale_bits >> 8).astype(np.uint8)
+    out[..., 2:] = nib[..., :16] | (nib[..., 16:] << 4)
+    return out.reshape(lead + (nb * Q4_BLOCK_BYTES,))
+
+
+def random_kv_rows_q4_0(rng: np.random.Generator, n_rows: int, n_head_kv: int, head_dim: int,
+                        scale_lo: float = 0.08, scale_hi: float = 0.32):
+    """One q4_0 tensor (V) of n_rows token rows -> uint8 [n_rows, row_bytes_q4_0].
+    Codes uniform over 0..15; the default scales (16x the q8_0 ones) give values
+    d * (code - 8) over the same range as the q8_0 rows."""
+    nb = n_head_kv * head_dim // QK
+    nib = rng.integers(0, 16, size=(n_rows, nb, QK), dtype=np.uint8)
+    scales = rng.uniform(scale_lo, scale_hi, size=(n_rows, nb)).astype(np.float16)
+    return pack_q4_0(nib, scales.view(np.uint16))
+
+
 def random_q(rng: np.random.Generator, n_seq: int, n_head_q: int, head_dim: int) -> np.ndarray:
     return rng.standard_normal(size=(n_seq, n_head_q, head_dim)).astype(np.float32)
 
