@@ -292,6 +292,62 @@ def residency(args, torch, kvd, inputs, link):
     return res
 
 
+def asymmetric(args, torch, kvd, inputs, link):
+    """q8_0 K with q4_0 V: the 16384-row, 64-layer host-resident stack (ordered vs
+    pipelined, 128 MiB ring), and the device-resident 4096-row call."""
+    from decode_attention_offloaded_amd import stack
+    c = inputs.config(2)
+    res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1),
+                                  budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log, v_type=1)
+    peak = max(link.values())
+    res["link_peak_GBps"] = peak
+    for arm in res["arms"].values():
+        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    # device-resident 4096 rows, 64 distinct layers per graph, a query per layer
+    c1 = inputs.config(1)
+    dev = torch.device("cuda:0")
+    L, n = 64, c1.n_ctx
+    vrb = inputs.row_bytes_q4_0(c1.n_head_kv, c1.head_dim)
+    ks, vs, qs = [], [], []
+    for l in range(L):
+        r = np.random.default_rng([c1.seed, 900 + l])
+        ks.append(torch.from_numpy(inputs.random_kv_rows(r, n, c1.n_head_kv, c1.head_dim)).to(dev))
+        vs.append(torch.from_numpy(inputs.random_kv_rows_q4_0(r, n, c1.n_head_kv, c1.head_dim)).to(dev))
+        qs.append(torch.from_numpy(inputs.random_q(r, 1, c1.n_head_q, c1.head_dim)).to(dev))
+    out = torch.empty_like(qs[0])
+    stream = torch.cuda.Stream(device=dev)
+    ws = kvd.Workspace()
+    def call(l):
+        kvd.attend_decode(qs[l], out, [[(ks[l], vs[l], 0)]], c1.n_head_kv, workspace=ws, stream=stream,
+                          v_type=kvd.TYPE_Q4_0)
+    with torch.cuda.stream(stream):
+        for l in range(L):
+            call(l)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for l in range(L):
+            call(l)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * L)
+    b = n * (c1.row_bytes + vrb) + 2 * c1.n_head_q * c1.head_dim * 4
+    res["device_4096"] = {"us_per_launch": round(us, 3), "bytes_per_launch": b,
+                          "GBps": round(b / (us * 1e-6) / 1e9, 1), "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log("asymmetric q8_0 K / q4_0 V: stack %s; 4096-row call %.2f us" % (
+        {k: (v["ms_per_token"], v["staged_GBps"]) for k, v in res["arms"].items()}, us))
+    return res
+
+
 def long_context(args, torch, kvd, inputs):
     """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
     from decode_attention_offloaded_amd import stack
@@ -394,6 +450,7 @@ def main():
     ap.add_argument("--residency", type=int, default=1, help="run the 131072-row residency-planner arms")
     ap.add_argument("--residency-layers", type=int, default=64)
     ap.add_argument("--residency-tokens", type=int, default=3)
+    ap.add_argument("--asym", type=int, default=1, help="run the q8_0 K / q4_0 V legs")
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
@@ -432,7 +489,7 @@ def main():
         "device_curve": d["curve"],
         "calibration_copy_bytes": calib,
     }
-    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency) else None
+    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym) else None
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
     if args.batched:
@@ -441,6 +498,8 @@ def main():
         out["tiled"] = tiled(args, torch, kvd, inputs, link)
     if args.residency:
         out["residency"] = residency(args, torch, kvd, inputs, link)
+    if args.asym:
+        out["asymmetric"] = asymmetric(args, torch, kvd, inputs, link)
     if args.long:
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:

@@ -59,7 +59,7 @@ struct SegDesc {
     int32_t n_vis;    // visible rows
     int32_t n_split;  // splits over this segment
     int32_t n_rows;   // readable rows
-    int32_t pad;
+    int32_t vstride;  // V row stride in bytes (q4_0 V rows are shorter)
 };
 
 struct SeqDesc {
@@ -611,7 +611,39 @@ __device__ inline void store_win(const uint32_t (&r)[9], uint32_t* t, int lane) 
     for (int i = 0; i < 9; ++i) t[64 * i + lane] = r[i];
 }
 
-template <int D, int G, int ODD>
+// V windows: q8_0 V as K (9 dwords around the 34-byte block); q4_0 V: 5
+// dwords around the 18-byte block, 64 rows x 5 dwords = 5 loads per lane
+// (unit 64 i + lane -> row = unit / 5, dword = unit % 5).
+template <int VT>
+struct VWin {
+    static constexpr int W = VT ? 5 : 9;        // dwords per row window
+    static constexpr int BB = VT ? 18 : 34;     // bytes per block
+};
+
+template <int VW>
+__device__ inline void load_vwin(uint32_t (&r)[VW], __amdgpu_buffer_rsrc_t rs, const int32_t (&voff)[VW]) {
+#pragma unroll
+    for (int i = 0; i < VW; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0);
+}
+
+template <int VW>
+__device__ inline void store_vwin(const uint32_t (&r)[VW], uint32_t* t, int lane) {
+#pragma unroll
+    for (int i = 0; i < VW; ++i) t[64 * i + lane] = r[i];
+}
+
+// Descriptor for head g of the V tile at row0 (V rows of their own stride and
+// block size); loads past the segment return zero.
+template <int D, int VT>
+__device__ inline __amdgpu_buffer_rsrc_t vtile_rsrc(const SegDesc& sg, int g, int row0) {
+    constexpr int CBV = (D / 32) * VWin<VT>::BB;
+    const int64_t head_off = (int64_t)row0 * sg.vstride + (int64_t)g * CBV;
+    const int64_t lim64 = (int64_t)(sg.n_rows - 1 - row0) * sg.vstride + CBV;
+    const int32_t lim = (int32_t)(lim64 > 0x7fffffff ? 0x7fffffff : lim64);
+    return make_rsrc(sg.v + head_off, lim);
+}
+
+template <int D, int G, int VT, int ODD>
 __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int g,
                                            const int r_begin, const int r_end, const bool single,
                                            const int abs_split, const int wave, const int lane, uint32_t* tk,
@@ -622,6 +654,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     const int n_head_q = A.n_head_kv * G;
     const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
 
+    constexpr int VW = VWin<VT>::W;
     int32_t voff[9];
     {
         const int32_t base = win_dword(wave) * 4;
@@ -631,12 +664,24 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             voff[i] = (7 * i + u / 9) * SG.stride + (u % 9) * 4 + base;
         }
     }
+    int32_t voffv[VW];
+    {
+        const int32_t base = ((VWin<VT>::BB * wave) >> 2) * 4;
+#pragma unroll
+        for (int i = 0; i < VW; ++i) {
+            const int u = 64 * i + lane;
+            voffv[i] = (u / VW) * SG.vstride + (u % VW) * 4 + base;
+        }
+    }
 
-    float m[G], l[G], o[G][4];
+    // q4_0 V: o accumulates c * code over the unsigned 4-bit codes and cs the
+    // weights c, so that o - 8 * cs is the sum over c * (code - 8)
+    float m[G], l[G], o[G][4], cs[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         m[h] = -INFINITY;
         l[h] = 0.f;
+        cs[h] = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
     }
@@ -652,9 +697,9 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     // serialise on its misses: several microseconds per call.)
     float4 qv4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (lane < G * 8) qv4 = *(const float4*)(qg + (lane >> 3) * D + 4 * (lane & 7));
-    uint32_t rk[9], rv[9];
+    uint32_t rk[9], rv[VW];
     load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
-    load_win(rv, tile_rsrc<D>(SG.v, SG, g, r_begin), voff);
+    load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, r_begin), voffv);
     if (lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
     store_win(rk, tk, lane);
 
@@ -715,8 +760,8 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             for (int h = 0; h < G; ++h) sxt[(wave * G + h) * 64 + lane] = dot[h] * dk;
         }
         lds_barrier();
-        store_win(rv, tv, lane);
-        if (has_next) load_win(rv, tile_rsrc<D>(SG.v, SG, g, row0 + T), voff);
+        store_vwin<VW>(rv, tv, lane);
+        if (has_next) load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, row0 + T), voffv);
         wave_lds_sync();
 
         // ---- full scores (same sum order in every wave) and online softmax
@@ -739,6 +784,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
                     if (mn > m[h]) {
                         const float alpha = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
                         l[h] *= alpha;
+                        if (VT) cs[h] *= alpha;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) o[h][e] *= alpha;
                         m[h] = mn;
@@ -748,7 +794,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
         }
         {
             // rows past the visible range may hold any bits: their weight is an exact 0
-            const float dv = (lane < nv) ? (ODD ? half_hi(tv[lane * 9]) : half_lo(tv[lane * 9])) : 0.f;
+            const float dv = (lane < nv) ? (ODD ? half_hi(tv[lane * VW]) : half_lo(tv[lane * VW])) : 0.f;
             float c[GP];
 #pragma unroll
             for (int h = 0; h < GP; ++h) c[h] = 0.f;
@@ -757,6 +803,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
                 const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
                 l[h] += p;
                 c[h] = p * dv;
+                if (VT) cs[h] += c[h];
             }
 #pragma unroll
             for (int h = 0; h < GP; h += 4) *(float4*)&scw[lane * GP + h] = make_float4(c[h], c[h + 1], c[h + 2], c[h + 3]);
@@ -767,8 +814,18 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
 #pragma unroll 4
         for (int ps = 0; ps < 8; ++ps) {
             const int r = ps * 8 + slot;
-            const uint32_t* rp = tv + r * 9;
-            const uint32_t x = ODD ? rp[grp + 1] : __builtin_amdgcn_alignbyte(rp[grp + 1], rp[grp], 2);
+            uint32_t x;
+            if constexpr (VT == 0) {
+                const uint32_t* rp = tv + r * 9;
+                x = ODD ? rp[grp + 1] : __builtin_amdgcn_alignbyte(rp[grp + 1], rp[grp], 2);
+            } else {
+                // dims 4 grp .. 4 grp + 3: low nibbles of code bytes 4 grp .. (grp < 4),
+                // high nibbles of bytes 4 (grp - 4) .. (grp >= 4)
+                const uint32_t* rp = tv + r * 5;
+                const int kq = grp & 3;
+                const uint32_t raw = ODD ? rp[kq + 1] : __builtin_amdgcn_alignbyte(rp[kq + 1], rp[kq], 2);
+                x = (raw >> ((grp >> 2) * 4)) & 0x0F0F0F0Fu;
+            }
             float c[GP];
 #pragma unroll
             for (int h = 0; h < GP; h += 4) {
@@ -780,7 +837,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float vv = sbyte(x, e);
+                const float vv = VT ? (float)((x >> (8 * e)) & 0xFFu) : sbyte(x, e);
 #pragma unroll
                 for (int h = 0; h < G; ++h) o[h][e] = fmaf(c[h], vv, o[h][e]);
             }
@@ -801,6 +858,11 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             o[h][e] = x;
         }
         l[h] = wave_sum(l[h]);
+        if (VT) {
+            const float c8 = 8.f * wave_sum(cs[h]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[h][e] -= c8;
+        }
     }
     const int hq0 = g * G;
     const int dim0 = 32 * wave + 4 * grp;
@@ -836,7 +898,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     }
 }
 
-template <int D, int G>
+template <int D, int G, int VT>
 __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A) {
     using S_ = Slice<D, G>;
     constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
@@ -867,11 +929,11 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
     const bool single = SQ.n_split == 1;
     const int abs_split = A.split_off + lsplit;
     if (wave & 1)
-        slice_body<D, G, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                            s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
+        slice_body<D, G, VT, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+                                s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
     else
-        slice_body<D, G, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                            s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
+        slice_body<D, G, VT, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+                                s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
 }
 
 // Merge n partial results (m_k, l_k, o_k) of one (sequence, query head) in
@@ -998,22 +1060,25 @@ decode_fn pick_decode(int D, int G, int NW) {
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
-template <int D>
+template <int D, int VT>
 decode_fn pick_slice_g(int G) {
     switch (G) {
-        case 1: return slice_kernel<D, 1>;
-        case 2: return slice_kernel<D, 2>;
-        case 3: return slice_kernel<D, 3>;
-        case 4: return slice_kernel<D, 4>;
-        case 5: return slice_kernel<D, 5>;
-        case 6: return slice_kernel<D, 6>;
-        case 7: return slice_kernel<D, 7>;
-        case 8: return slice_kernel<D, 8>;
+        case 1: return slice_kernel<D, 1, VT>;
+        case 2: return slice_kernel<D, 2, VT>;
+        case 3: return slice_kernel<D, 3, VT>;
+        case 4: return slice_kernel<D, 4, VT>;
+        case 5: return slice_kernel<D, 5, VT>;
+        case 6: return slice_kernel<D, 6, VT>;
+        case 7: return slice_kernel<D, 7, VT>;
+        case 8: return slice_kernel<D, 8, VT>;
     }
     return nullptr;
 }
 
-decode_fn pick_slice(int D, int G) { return D == 128 ? pick_slice_g<128>(G) : pick_slice_g<64>(G); }
+decode_fn pick_slice(int D, int G, int VT) {
+    if (VT) return D == 128 ? pick_slice_g<128, 1>(G) : pick_slice_g<64, 1>(G);
+    return D == 128 ? pick_slice_g<128, 0>(G) : pick_slice_g<64, 0>(G);
+}
 
 }  // namespace
 }  // namespace kvd
@@ -1048,7 +1113,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    const decode_fn dk = p.kernel == 3 ? pick_slice(a->head_dim, p.group) : pick_decode(a->head_dim, p.group, p.waves);
+    const decode_fn dk = p.kernel == 3 ? pick_slice(a->head_dim, p.group, a->v_type) : pick_decode(a->head_dim, p.group, p.waves);
     const combine_fn ck = pick_combine(a->head_dim);
     if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 
@@ -1078,6 +1143,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                     sd.k = (const uint8_t*)segs[k].k;
                     sd.v = (const uint8_t*)segs[k].v;
                     sd.stride = (int32_t)segs[k].row_stride;
+                    sd.vstride = (int32_t)(segs[k].v_row_stride ? segs[k].v_row_stride : segs[k].row_stride);
                 }
             }
             d.split_base = (int32_t)(sp.split_base - base0);

@@ -33,10 +33,15 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     if (!a->q || !a->segs) return fail(KVD_EINVAL, "q and segs must not be NULL");
     if ((uintptr_t)a->q % 16) return fail(KVD_EINVAL, "q must be 16-byte aligned");
 
+    if (a->v_type != KVD_TYPE_Q8_0 && a->v_type != KVD_TYPE_Q4_0)
+        return fail(KVD_EINVAL, "v_type %d must be KVD_TYPE_Q8_0 or KVD_TYPE_Q4_0", a->v_type);
     const int D = a->head_dim;
     const int chunk = D / 32 * 34;
     const int64_t row_bytes = (int64_t)a->n_head_kv * chunk;
+    const int64_t v_row_bytes = (int64_t)a->n_head_kv * (D / 32) * (a->v_type == KVD_TYPE_Q4_0 ? 18 : 34);
     const int64_t align = (D == 128) ? 8 : 4;
+    const int64_t v_align = a->v_type == KVD_TYPE_Q4_0 ? 4 : align;
+    bool strides_differ = false;
 
     p->group = G;
     p->chunk_bytes = chunk;
@@ -56,9 +61,17 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
             if (g.row_stride < row_bytes || g.row_stride >= ((int64_t)1 << 25))
                 return fail(KVD_EINVAL, "seq %d seg %d: row_stride %lld (row bytes %lld, limit 2^25)", s, j,
                             (long long)g.row_stride, (long long)row_bytes);
-            if ((uintptr_t)g.k % align || (uintptr_t)g.v % align || g.row_stride % align)
-                return fail(KVD_EINVAL, "seq %d seg %d: k, v and row_stride must be %lld-byte aligned", s, j,
+            if ((uintptr_t)g.k % align || g.row_stride % align)
+                return fail(KVD_EINVAL, "seq %d seg %d: k and row_stride must be %lld-byte aligned", s, j,
                             (long long)align);
+            const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
+            if (g.v_row_stride < 0 || vs < v_row_bytes || vs >= ((int64_t)1 << 25))
+                return fail(KVD_EINVAL, "seq %d seg %d: V row stride %lld (V row bytes %lld, limit 2^25)", s, j,
+                            (long long)vs, (long long)v_row_bytes);
+            if ((uintptr_t)g.v % v_align || vs % v_align)
+                return fail(KVD_EINVAL, "seq %d seg %d: v and its row stride must be %lld-byte aligned", s, j,
+                            (long long)v_align);
+            strides_differ |= vs != g.row_stride;
         }
         const kvd_kv_seg& last = segs[a->n_seg - 1];
         int64_t qp;
@@ -105,6 +118,8 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // longer splits keep the merge small.
     const int64_t work = total_sub * a->n_head_kv;
     p->kernel = kKernelChoice != 0 ? kKernelChoice : (work <= kSliceMaxWork ? 3 : 1);
+    // only the block-sliced kernel reads q4_0 V or V rows of their own stride
+    if (a->v_type != KVD_TYPE_Q8_0 || strides_differ) p->kernel = 3;
     p->waves = p->kernel == 3 ? a->head_dim / 32 : (work >= kTargetWaves) ? 8 : 2;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {

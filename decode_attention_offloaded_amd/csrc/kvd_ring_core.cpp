@@ -7,12 +7,12 @@
 
 namespace kvd {
 
-bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t* need) {
+bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t v_row_bytes, int64_t* need) {
     if (depth <= 0) {
         *need = 0;
         return true;
     }
-    const __int128 x = (__int128)(depth + 2) * 2 * (__int128)cap_rows * (__int128)row_bytes;
+    const __int128 x = (__int128)(depth + 2) * (__int128)cap_rows * ((__int128)row_bytes + (__int128)v_row_bytes);
     if (x < 0 || x > (__int128)INT64_MAX) return false;
     *need = (int64_t)x;
     return true;
@@ -36,6 +36,9 @@ int Ring::validate(const kvd_stage_args* a) const {
     if (!a->host_k || !a->host_v) return fail(KVD_EINVAL, "host_k/host_v must not be NULL");
     if (a->row_bytes <= 0 || a->row_bytes % 4 != 0 || a->row_bytes > (1 << 24))
         return fail(KVD_EINVAL, "row_bytes %lld must be a positive multiple of 4 (< 2^24)", (long long)a->row_bytes);
+    if (a->v_row_bytes < 0 || a->v_row_bytes % 4 != 0 || a->v_row_bytes > (1 << 24))
+        return fail(KVD_EINVAL, "v_row_bytes %lld must be 0 or a positive multiple of 4 (< 2^24)",
+                    (long long)a->v_row_bytes);
     if (a->cap_rows < 1 || a->cap_rows >= ((int64_t)1 << 31))
         return fail(KVD_EINVAL, "cap_rows %lld out of range", (long long)a->cap_rows);
     if (a->n_rows < 1 || a->n_rows > a->cap_rows)
@@ -74,15 +77,15 @@ void Ring::free_resources() {
     }
 }
 
-int Ring::engage(int64_t slot_bytes) {
+int Ring::engage(int64_t k_bytes, int64_t v_bytes) {
     slots_.assign(n_slots_, Slot());
     bool ok = true;
     for (StreamH& x : xfer_) ok = ok && t_->stream_create(&x) == 0;
     for (int i = 0; ok && i < n_slots_; ++i) {
         Slot& s = slots_[i];
         for (EventH& e : s.ready) ok = ok && t_->event_create(&e) == 0;
-        ok = ok && t_->event_create(&s.rel) == 0 && t_->alloc((size_t)slot_bytes, &s.k) == 0 &&
-             t_->alloc((size_t)slot_bytes, &s.v) == 0;
+        ok = ok && t_->event_create(&s.rel) == 0 && t_->alloc((size_t)k_bytes, &s.k) == 0 &&
+             t_->alloc((size_t)v_bytes, &s.v) == 0;
     }
     if (!ok) {
         // a failed allocation is a decline, not an error: undo everything
@@ -90,10 +93,11 @@ int Ring::engage(int64_t slot_bytes) {
         return KVD_ENOMEM;
     }
     engaged_ = true;
-    slot_bytes_ = slot_bytes;
+    slot_bytes_ = k_bytes;
+    slot_v_bytes_ = v_bytes;
     cursor_ = 0;
     last_xfer_ = 0;
-    st_.ring_bytes = 2 * (int64_t)n_slots_ * slot_bytes;
+    st_.ring_bytes = (int64_t)n_slots_ * (k_bytes + v_bytes);
     return KVD_OK;
 }
 
@@ -106,6 +110,7 @@ void Ring::teardown() {
     free_resources();
     engaged_ = false;
     slot_bytes_ = 0;
+    slot_v_bytes_ = 0;
     cursor_ = 0;
     last_xfer_ = 0;
     st_.ring_bytes = 0;
@@ -114,7 +119,7 @@ void Ring::teardown() {
 int Ring::plan(const kvd_stage_args* a) {
     if (depth_ == 0 || declined_) return KVD_DECLINED;
     int64_t need;
-    if (!ring_need_bytes(depth_, a->cap_rows, a->row_bytes, &need)) need = INT64_MAX;
+    if (!ring_need_bytes(depth_, a->cap_rows, a->row_bytes, v_row_bytes_of(a), &need)) need = INT64_MAX;
     need_ = need;
     st_.need_bytes = need;
     int dev = -1;
@@ -131,12 +136,13 @@ int Ring::plan(const kvd_stage_args* a) {
         return KVD_DECLINED;
     }
     const int64_t slot_bytes = a->cap_rows * a->row_bytes;
-    if (engaged_ && slot_bytes > slot_bytes_) {
+    const int64_t slot_v_bytes = a->cap_rows * v_row_bytes_of(a);
+    if (engaged_ && (slot_bytes > slot_bytes_ || slot_v_bytes > slot_v_bytes_)) {
         if (busy()) return fail(KVD_ESTATE, "slot capacity grew while deliveries are in flight");
         teardown();
     }
     if (!engaged_) {
-        if (engage(slot_bytes) != KVD_OK) {
+        if (engage(slot_bytes, slot_v_bytes) != KVD_OK) {
             declined_ = true;
             return KVD_DECLINED;
         }
@@ -156,13 +162,13 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
                     s, S.layer, a->layer);
     // stream to stream: the copies wait for the release of the slot's previous
     // layer, recorded earlier in host order on the compute stream
-    const size_t bytes = (size_t)rows * (size_t)a->row_bytes;
+    const size_t bytes[kXferStreams] = {(size_t)rows * (size_t)a->row_bytes, (size_t)rows * (size_t)v_row_bytes_of(a)};
     void* dst[kXferStreams] = {S.k, S.v};
     const void* src[kXferStreams] = {a->host_k, a->host_v};
     for (int x = 0; x < kXferStreams; ++x) {
         if (S.released_once && t_->wait(xfer_[x], S.rel) != 0)
             return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
-        if (bytes > 0 && t_->copy_h2d(dst[x], src[x], bytes, xfer_[x]) != 0)
+        if (bytes[x] > 0 && t_->copy_h2d(dst[x], src[x], bytes[x], xfer_[x]) != 0)
             return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
         if (t_->record(S.ready[x], xfer_[x]) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
     }
@@ -170,6 +176,7 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
     S.layer = a->layer;
     S.prefix_rows = rows;
     S.row_bytes = a->row_bytes;
+    S.v_row_bytes = v_row_bytes_of(a);
     S.host_k = a->host_k;
     S.host_v = a->host_v;
     S.delivery = cursor_;
@@ -181,13 +188,14 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
 
 int Ring::ordered_acquire(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
     if (!a->ordered_k || !a->ordered_v) return fail(KVD_EINVAL, "the ordered path needs ordered_k and ordered_v");
-    const size_t bytes = (size_t)a->n_rows * (size_t)a->row_bytes;
-    if (t_->copy_h2d(a->ordered_k, a->host_k, bytes, compute) != 0 ||
-        t_->copy_h2d(a->ordered_v, a->host_v, bytes, compute) != 0)
+    const size_t kb = (size_t)a->n_rows * (size_t)a->row_bytes;
+    const size_t vb = (size_t)a->n_rows * (size_t)v_row_bytes_of(a);
+    if (t_->copy_h2d(a->ordered_k, a->host_k, kb, compute) != 0 ||
+        t_->copy_h2d(a->ordered_v, a->host_v, vb, compute) != 0)
         return fail(KVD_EHIP, "ordered copy: %s", t_->error_text());
     st_.n_acquire_ordered++;
-    st_.bytes_ordered += 2 * (int64_t)bytes;
-    if (out) *out = kvd_slot_view{a->ordered_k, a->ordered_v, a->n_rows, a->row_bytes, 0, -1};
+    st_.bytes_ordered += (int64_t)(kb + vb);
+    if (out) *out = kvd_slot_view{a->ordered_k, a->ordered_v, a->n_rows, a->row_bytes, 0, -1, v_row_bytes_of(a)};
     return KVD_DECLINED;
 }
 
@@ -195,14 +203,14 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
     int rc = validate(a);
     if (rc != KVD_OK) return rc;
     int pinned = 0;
-    const size_t span = (size_t)a->n_rows * (size_t)a->row_bytes;
-    if (t_->host_pinned(a->host_k, span, &pinned) != 0 || !pinned)
+    const int64_t vrb = v_row_bytes_of(a);
+    if (t_->host_pinned(a->host_k, (size_t)a->n_rows * (size_t)a->row_bytes, &pinned) != 0 || !pinned)
         return fail(KVD_EINVAL, "host_k is not pinned host memory");
-    if (t_->host_pinned(a->host_v, span, &pinned) != 0 || !pinned)
+    if (t_->host_pinned(a->host_v, (size_t)a->n_rows * (size_t)vrb, &pinned) != 0 || !pinned)
         return fail(KVD_EINVAL, "host_v is not pinned host memory");
 
     if (a->flags == KVD_STAGE_PREFETCH) {
-        if (out) *out = kvd_slot_view{nullptr, nullptr, 0, 0, 0, -1};
+        if (out) *out = kvd_slot_view{nullptr, nullptr, 0, 0, 0, -1, 0};
         rc = plan(a);
         if (rc != KVD_OK) return rc;  // KVD_DECLINED: nothing to do
         if (find_layer(a->layer, STAGED) >= 0 || find_layer(a->layer, ACQUIRED) >= 0)
@@ -211,7 +219,7 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
         rc = deliver_prefix(a, a->stable_rows, &s);
         if (rc != KVD_OK) return rc;
         st_.n_prefetch++;
-        st_.bytes_early += 2 * a->stable_rows * a->row_bytes;
+        st_.bytes_early += a->stable_rows * (a->row_bytes + vrb);
         return KVD_OK;
     }
 
@@ -226,10 +234,10 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
         rc = deliver_prefix(a, a->n_rows, &s);
         if (rc != KVD_OK) return rc;
         st_.n_acquire_primed++;
-        st_.bytes_late += 2 * a->n_rows * a->row_bytes;
+        st_.bytes_late += a->n_rows * (a->row_bytes + vrb);
     } else {
         Slot& S = slots_[s];
-        if (S.row_bytes != a->row_bytes || S.host_k != a->host_k || S.host_v != a->host_v)
+        if (S.row_bytes != a->row_bytes || S.v_row_bytes != vrb || S.host_k != a->host_k || S.host_v != a->host_v)
             return fail(KVD_ESTATE, "ACQUIRE of layer %d does not match its PREFETCH (host buffers or row_bytes)",
                         a->layer);
         if (a->n_rows < S.prefix_rows)
@@ -237,25 +245,27 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
                         (long long)a->n_rows, (long long)S.prefix_rows);
         const int64_t tail = a->n_rows - S.prefix_rows;
         if (tail > 0) {
-            const size_t off = (size_t)S.prefix_rows * (size_t)a->row_bytes;
-            const size_t n = (size_t)tail * (size_t)a->row_bytes;
-            void* dk = (uint8_t*)S.k + off;
-            void* dv = (uint8_t*)S.v + off;
-            const void* hk = (const uint8_t*)a->host_k + off;
-            const void* hv = (const uint8_t*)a->host_v + off;
+            const size_t koff = (size_t)S.prefix_rows * (size_t)a->row_bytes;
+            const size_t voff = (size_t)S.prefix_rows * (size_t)vrb;
+            const size_t kn = (size_t)tail * (size_t)a->row_bytes;
+            const size_t vn = (size_t)tail * (size_t)vrb;
+            void* dk = (uint8_t*)S.k + koff;
+            void* dv = (uint8_t*)S.v + voff;
+            const void* hk = (const uint8_t*)a->host_k + koff;
+            const void* hv = (const uint8_t*)a->host_v + voff;
             if (last_xfer_ == S.delivery + 1) {
                 // this layer's prefix is the newest work on the transfer streams:
                 // the tail follows it there and `ready` moves behind the tail
-                if (t_->copy_h2d(dk, hk, n, xfer_[0]) != 0 || t_->record(S.ready[0], xfer_[0]) != 0 ||
-                    t_->copy_h2d(dv, hv, n, xfer_[1]) != 0 || t_->record(S.ready[1], xfer_[1]) != 0)
+                if (t_->copy_h2d(dk, hk, kn, xfer_[0]) != 0 || t_->record(S.ready[0], xfer_[0]) != 0 ||
+                    t_->copy_h2d(dv, hv, vn, xfer_[1]) != 0 || t_->record(S.ready[1], xfer_[1]) != 0)
                     return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
             } else {
                 // later prefixes are queued on the transfer stream: do not wait
                 // behind them, copy the tail on the compute stream
-                if (t_->copy_h2d(dk, hk, n, compute) != 0 || t_->copy_h2d(dv, hv, n, compute) != 0)
+                if (t_->copy_h2d(dk, hk, kn, compute) != 0 || t_->copy_h2d(dv, hv, vn, compute) != 0)
                     return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
             }
-            st_.bytes_late += 2 * (int64_t)n;
+            st_.bytes_late += (int64_t)(kn + vn);
         }
         st_.n_acquire_pipelined++;
     }
@@ -263,7 +273,7 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
     for (EventH e : S.ready)
         if (t_->wait(compute, e) != 0) return fail(KVD_EHIP, "wait(ready): %s", t_->error_text());
     S.state = ACQUIRED;
-    if (out) *out = kvd_slot_view{S.k, S.v, a->n_rows, a->row_bytes, 1, s};
+    if (out) *out = kvd_slot_view{S.k, S.v, a->n_rows, a->row_bytes, 1, s, vrb};
     return KVD_OK;
 }
 
@@ -283,7 +293,7 @@ void Ring::stats(kvd_ring_stats* out) const {
     out->engaged = engaged_ ? 1 : 0;
     out->declined = declined_ ? 1 : 0;
     out->device = engaged_ ? device_ : -1;
-    out->ring_bytes = engaged_ ? 2 * (int64_t)n_slots_ * slot_bytes_ : 0;
+    out->ring_bytes = engaged_ ? (int64_t)n_slots_ * (slot_bytes_ + slot_v_bytes_) : 0;
 }
 
 }  // namespace kvd
@@ -334,7 +344,7 @@ extern "C" int kvd_ring_tile_rows(int32_t depth, size_t budget_bytes, int64_t ro
     rows = rows / 64 * 64;
     if (rows > ((int64_t)1 << 30)) rows = (int64_t)1 << 30;
     int64_t need = 0;
-    while (rows > 0 && (!ring_need_bytes(depth, rows, row_bytes, &need) || need > budget)) rows -= 64;
+    while (rows > 0 && (!ring_need_bytes(depth, rows, row_bytes, row_bytes, &need) || need > budget)) rows -= 64;
     if (rows < 64) return KVD_DECLINED;
     *tile_rows = rows;
     return KVD_OK;

@@ -45,9 +45,12 @@ public:
     virtual const char* error_text() = 0;
 };
 
-// Ring size for depth N: N + 2 slots, each K and V of cap_rows rows.
+// Ring size for depth N: N + 2 slots, each cap_rows K rows and cap_rows V rows.
 // Returns false on overflow.  Depth 0 has no ring (need = 0).
-bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t* need);
+bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t v_row_bytes, int64_t* need);
+
+// Bytes of one V row of a stage call (0 in the arguments means = row_bytes).
+inline int64_t v_row_bytes_of(const kvd_stage_args* a) { return a->v_row_bytes ? a->v_row_bytes : a->row_bytes; }
 
 // Transfer streams per ring: K rows go on one, V rows on the other, so two
 // DMA engines copy in parallel (one engine tops out below the host link, and
@@ -76,6 +79,7 @@ private:
         int32_t layer = -1;
         int64_t prefix_rows = 0;
         int64_t row_bytes = 0;
+        int64_t v_row_bytes = 0;
         const void* host_k = nullptr;
         const void* host_v = nullptr;
         uint64_t delivery = 0;  // cursor value of the current delivery
@@ -86,7 +90,7 @@ private:
     // Decide ordered vs ring for this call; allocates lazily.  Returns KVD_OK
     // (ring usable), KVD_DECLINED (ordered path), or an error.
     int plan(const kvd_stage_args* a);
-    int engage(int64_t slot_bytes);
+    int engage(int64_t k_bytes, int64_t v_bytes);
     void free_resources();
     bool busy() const;  // any slot STAGED or ACQUIRED
     int find_layer(int32_t layer, int state) const;
@@ -100,7 +104,8 @@ private:
     bool declined_ = false;
     bool engaged_ = false;
     int device_ = -1;
-    int64_t slot_bytes_ = 0;  // bytes per K (and per V) buffer of a slot
+    int64_t slot_bytes_ = 0;    // bytes of the K buffer of a slot
+    int64_t slot_v_bytes_ = 0;  // bytes of the V buffer of a slot
     int64_t need_ = 0;
     StreamH xfer_[kXferStreams] = {nullptr, nullptr};
     std::vector<Slot> slots_;

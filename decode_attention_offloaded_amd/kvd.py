@@ -22,11 +22,13 @@ KVD_EHIP = -3
 KVD_ESTATE = -4
 STAGE_PREFETCH = 1
 STAGE_ACQUIRE = 2
+TYPE_Q8_0 = 0
+TYPE_Q4_0 = 1
 
 
 class KvSeg(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_rows", ctypes.c_int64),
-                ("pos0", ctypes.c_int64), ("row_stride", ctypes.c_int64)]
+                ("pos0", ctypes.c_int64), ("row_stride", ctypes.c_int64), ("v_row_stride", ctypes.c_int64)]
 
 
 class AttnArgs(ctypes.Structure):
@@ -34,19 +36,21 @@ class AttnArgs(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("n_seg", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("split_rows", ctypes.c_int32), ("scale", ctypes.c_float), ("q", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("segs", ctypes.POINTER(KvSeg)), ("q_pos", ctypes.POINTER(ctypes.c_int64)),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t), ("v_type", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class StageArgs(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_int32), ("flags", ctypes.c_int32), ("host_k", ctypes.c_void_p),
                 ("host_v", ctypes.c_void_p), ("row_bytes", ctypes.c_int64), ("n_rows", ctypes.c_int64),
                 ("stable_rows", ctypes.c_int64), ("cap_rows", ctypes.c_int64), ("ordered_k", ctypes.c_void_p),
-                ("ordered_v", ctypes.c_void_p)]
+                ("ordered_v", ctypes.c_void_p), ("v_row_bytes", ctypes.c_int64)]
 
 
 class SlotView(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_rows", ctypes.c_int64),
-                ("row_stride", ctypes.c_int64), ("pipelined", ctypes.c_int32), ("slot", ctypes.c_int32)]
+                ("row_stride", ctypes.c_int64), ("pipelined", ctypes.c_int32), ("slot", ctypes.c_int32),
+                ("v_row_stride", ctypes.c_int64)]
 
 
 class ResidencyPlan(ctypes.Structure):
@@ -150,13 +154,14 @@ def _stream_handle(stream) -> int:
 # ------------------------------------------------------------------ attention
 
 def make_args(q, out, segs: Sequence[Sequence], n_head_kv: int, window: int = 0, scale: Optional[float] = None,
-              q_pos=None, split_rows: int = 0):
+              q_pos=None, split_rows: int = 0, v_type: int = TYPE_Q8_0):
     """Build kvd_attn_args from torch tensors.
 
     q, out : float32 CUDA tensors [n_seq, n_head_q, head_dim], contiguous.
     segs   : per sequence, a list of segments ``(k, v, pos0)``; k and v are uint8
-             CUDA tensors [n_rows, >= row_bytes] whose row stride (in bytes) is
-             k.stride(0); or ``(k_ptr, v_ptr, n_rows, pos0, row_stride)`` with raw
+             CUDA tensors [n_rows, >= row bytes] (row strides k.stride(0) and
+             v.stride(0); v narrower than k when v_type is TYPE_Q4_0); or
+             ``(k_ptr, v_ptr, n_rows, pos0, row_stride[, v_row_stride])`` with raw
              device addresses.
     Returns (AttnArgs, keepalive).
     """
@@ -171,21 +176,27 @@ def make_args(q, out, segs: Sequence[Sequence], n_head_kv: int, window: int = 0,
         for j, seg in enumerate(seq):
             if len(seg) == 3:
                 k, v, pos0 = seg
-                if k.dtype.itemsize != 1 or k.dim() != 2 or tuple(k.shape) != tuple(v.shape) or k.stride() != v.stride():
-                    raise ValueError("segment k/v must be 2-D byte tensors of one geometry")
-                if k.stride(1) != 1:
+                if k.dtype.itemsize != 1 or v.dtype.itemsize != 1 or k.dim() != 2 or v.dim() != 2:
+                    raise ValueError("segment k/v must be 2-D byte tensors")
+                if k.shape[0] != v.shape[0]:
+                    raise ValueError("segment k and v must have as many rows")
+                if v_type == TYPE_Q8_0 and (tuple(k.shape) != tuple(v.shape) or k.stride() != v.stride()):
+                    raise ValueError("q8_0 segment k/v must share one geometry")
+                if k.stride(1) != 1 or v.stride(1) != 1:
                     raise ValueError("segment rows must be contiguous")
-                arr[s * n_seg + j] = KvSeg(k.data_ptr(), v.data_ptr(), k.shape[0], int(pos0), k.stride(0))
+                arr[s * n_seg + j] = KvSeg(k.data_ptr(), v.data_ptr(), k.shape[0], int(pos0), k.stride(0),
+                                           v.stride(0))
             else:
-                kp, vp, n_rows, pos0, stride = seg
-                arr[s * n_seg + j] = KvSeg(int(kp), int(vp), int(n_rows), int(pos0), int(stride))
+                kp, vp, n_rows, pos0, stride = seg[:5]
+                vstride = seg[5] if len(seg) > 5 else 0
+                arr[s * n_seg + j] = KvSeg(int(kp), int(vp), int(n_rows), int(pos0), int(stride), int(vstride))
     qp = None
     if q_pos is not None:
         qp = (ctypes.c_int64 * n_seq)(*[int(x) for x in q_pos])
     if scale is None:
         scale = head_dim ** -0.5
     a = AttnArgs(n_seq, n_head_q, n_head_kv, head_dim, n_seg, int(window), int(split_rows), float(scale),
-                 q.data_ptr(), out.data_ptr(), arr, qp, None, 0)
+                 q.data_ptr(), out.data_ptr(), arr, qp, None, 0, int(v_type), 0)
     return a, (arr, qp)
 
 
@@ -217,14 +228,14 @@ _default_ws = Workspace()
 
 
 def attend_decode(q, out, segs, n_head_kv: int, window: int = 0, scale: Optional[float] = None, q_pos=None,
-                  split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None):
+                  split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None, v_type: int = TYPE_Q8_0):
     """Enqueue decode attention on ``stream`` (default: torch's current stream)."""
     import torch
     if not (q.is_cuda and out.is_cuda) or q.dtype != torch.float32 or out.dtype != torch.float32:
         raise ValueError("q and out must be float32 CUDA tensors")
     if not (q.is_contiguous() and out.is_contiguous()):
         raise ValueError("q and out must be contiguous")
-    a, keep = make_args(q, out, segs, n_head_kv, window, scale, q_pos, split_rows)
+    a, keep = make_args(q, out, segs, n_head_kv, window, scale, q_pos, split_rows, v_type)
     nbytes = workspace_bytes(a)
     ws = (workspace or _default_ws).get(nbytes, q.device)
     if ws is not None:
@@ -240,7 +251,8 @@ def partial_floats(n_seq: int, n_head_q: int, head_dim: int) -> int:
 
 
 def attend_decode_partial(q, partial, segs, n_head_kv: int, window: int = 0, scale: Optional[float] = None,
-                          q_pos=None, split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None):
+                          q_pos=None, split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None,
+                          v_type: int = TYPE_Q8_0):
     """Enqueue decode attention over these rows only, leaving the unnormalised
     result (o, m, l) in ``partial`` (a float32 CUDA tensor of at least
     partial_floats(...) elements, e.g. one row of a [n_part, ...] tensor)."""
@@ -252,7 +264,7 @@ def attend_decode_partial(q, partial, segs, n_head_kv: int, window: int = 0, sca
     n_seq, n_head_q, head_dim = q.shape
     if partial.numel() < partial_floats(n_seq, n_head_q, head_dim):
         raise ValueError("partial is too small")
-    a, keep = make_args(q, q, segs, n_head_kv, window, scale, q_pos, split_rows)
+    a, keep = make_args(q, q, segs, n_head_kv, window, scale, q_pos, split_rows, v_type)
     a.out = None
     nbytes = workspace_bytes(a)
     ws = (workspace or _default_ws).get(nbytes, q.device)
@@ -313,10 +325,12 @@ class Ring:
         self.depth = depth
 
     def stage(self, layer: int, flags: int, host_k: int, host_v: int, row_bytes: int, n_rows: int,
-              stable_rows: int, cap_rows: int, ordered_k: int = 0, ordered_v: int = 0, stream=None):
+              stable_rows: int, cap_rows: int, ordered_k: int = 0, ordered_v: int = 0, stream=None,
+              v_row_bytes: int = 0):
         """Returns (rc, SlotView); rc is KVD_OK or KVD_DECLINED, errors raise."""
         a = StageArgs(int(layer), int(flags), int(host_k), int(host_v), int(row_bytes), int(n_rows),
-                      int(stable_rows), int(cap_rows), int(ordered_k) or None, int(ordered_v) or None)
+                      int(stable_rows), int(cap_rows), int(ordered_k) or None, int(ordered_v) or None,
+                      int(v_row_bytes))
         view = SlotView()
         rc = lib().kvd_ring_stage_layer(self._h, ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream)),
                                         ctypes.byref(view))

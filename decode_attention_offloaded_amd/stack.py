@@ -60,37 +60,44 @@ class PinnedBuffer:
 
 
 class HostKV:
-    """K and V of n_layers layers, each [cap_rows][row_bytes], in pinned host memory."""
+    """K and V of n_layers layers, each [cap_rows][row_bytes] (V rows v_row_bytes
+    wide: shorter for a q4_0 V cache), in pinned host memory."""
 
-    def __init__(self, n_layers: int, cap_rows: int, row_bytes: int):
+    def __init__(self, n_layers: int, cap_rows: int, row_bytes: int, v_row_bytes: Optional[int] = None,
+                 v_type: int = 0):
         self.n_layers, self.cap_rows, self.row_bytes = n_layers, cap_rows, row_bytes
+        self.v_row_bytes = v_row_bytes or row_bytes
+        self.v_type = v_type
         self.layer_bytes = cap_rows * row_bytes
+        self.v_layer_bytes = cap_rows * self.v_row_bytes
         self.k = PinnedBuffer(n_layers * self.layer_bytes)
-        self.v = PinnedBuffer(n_layers * self.layer_bytes)
+        self.v = PinnedBuffer(n_layers * self.v_layer_bytes)
 
     def k_rows(self, layer):
         o = layer * self.layer_bytes
         return self.k.array[o:o + self.layer_bytes].reshape(self.cap_rows, self.row_bytes)
 
     def v_rows(self, layer):
-        o = layer * self.layer_bytes
-        return self.v.array[o:o + self.layer_bytes].reshape(self.cap_rows, self.row_bytes)
+        o = layer * self.v_layer_bytes
+        return self.v.array[o:o + self.v_layer_bytes].reshape(self.cap_rows, self.v_row_bytes)
 
     def k_ptr(self, layer):
         return self.k.ptr + layer * self.layer_bytes
 
     def v_ptr(self, layer):
-        return self.v.ptr + layer * self.layer_bytes
+        return self.v.ptr + layer * self.v_layer_bytes
 
     def fill(self, inputs, cfg, n_rows: int, distinct: Optional[int] = None):
-        """Seeded q8_0 rows.  With `distinct`, only that many layers are drawn and
-        the rest repeat them (keeps very large stacks quick to set up)."""
+        """Seeded q8_0 K rows and q8_0 (or q4_0) V rows.  With `distinct`, only that
+        many layers are drawn and the rest repeat them (keeps very large stacks
+        quick to set up)."""
         distinct = self.n_layers if distinct is None else min(distinct, self.n_layers)
+        vgen = inputs.random_kv_rows_q4_0 if self.v_type == 1 else inputs.random_kv_rows
         for l in range(self.n_layers):
             if l < distinct:
                 r = cfg.layer_rng(l)
                 self.k_rows(l)[:n_rows] = inputs.random_kv_rows(r, n_rows, cfg.n_head_kv, cfg.head_dim)
-                self.v_rows(l)[:n_rows] = inputs.random_kv_rows(r, n_rows, cfg.n_head_kv, cfg.head_dim)
+                self.v_rows(l)[:n_rows] = vgen(r, n_rows, cfg.n_head_kv, cfg.head_dim)
             else:
                 self.k_rows(l)[:n_rows] = self.k_rows(l % distinct)[:n_rows]
                 self.v_rows(l)[:n_rows] = self.v_rows(l % distinct)[:n_rows]
@@ -120,7 +127,7 @@ class Stack:
         self.ring = kvd.Ring(depth, budget_bytes)
         rb = host.row_bytes
         self.ordered_k = torch.empty(host.cap_rows * rb, dtype=torch.uint8, device=dev)
-        self.ordered_v = torch.empty(host.cap_rows * rb, dtype=torch.uint8, device=dev)
+        self.ordered_v = torch.empty(host.cap_rows * host.v_row_bytes, dtype=torch.uint8, device=dev)
         g = np.random.default_rng([cfg.seed, 7777])
         self.q = [torch.from_numpy(cfg_q(g, cfg)).to(dev) for _ in range(host.n_layers)]
         self.out = [torch.empty_like(self.q[0]) for _ in range(host.n_layers)]
@@ -138,7 +145,7 @@ class Stack:
         h = self.host
         return self.ring.stage(layer, flags, h.k_ptr(layer), h.v_ptr(layer), h.row_bytes, self.n_rows,
                                self.n_rows - 1, h.cap_rows, self.ordered_k.data_ptr(), self.ordered_v.data_ptr(),
-                               stream=self.stream)
+                               stream=self.stream, v_row_bytes=h.v_row_bytes)
 
     def token(self, t: int):
         """One decode token over every layer; returns the token time in ms (compute-stream events)."""
@@ -167,13 +174,14 @@ class Stack:
                         self.dev_k[l][self.n_rows - 1].copy_(kd)
                         self.dev_v[l][self.n_rows - 1].copy_(vd)
                     kvd.attend_decode(self.q[l], self.out[l], [[(self.dev_k[l], self.dev_v[l], 0)]],
-                                      self.cfg.n_head_kv, workspace=self.ws, stream=s)
+                                      self.cfg.n_head_kv, workspace=self.ws, stream=s, v_type=h.v_type)
                     continue
                 rc, view = self._stage(l, kvd.STAGE_ACQUIRE)
                 if self.on_view is not None:
                     self.on_view(l, view)
-                kvd.attend_decode(self.q[l], self.out[l], [[(view.k, view.v, view.n_rows, 0, view.row_stride)]],
-                                  self.cfg.n_head_kv, workspace=self.ws, stream=s)
+                kvd.attend_decode(self.q[l], self.out[l],
+                                  [[(view.k, view.v, view.n_rows, 0, view.row_stride, view.v_row_stride)]],
+                                  self.cfg.n_head_kv, workspace=self.ws, stream=s, v_type=h.v_type)
                 if self.after_attend is not None:
                     self.after_attend(l, view)
                 self.ring.release(l, stream=s)
@@ -193,13 +201,14 @@ def cfg_q(g, cfg):
     return g.standard_normal((1, cfg.n_head_q, cfg.head_dim)).astype(np.float32)
 
 
-def token_rows(cfg, pool: int = 4):
+def token_rows(cfg, pool: int = 4, v_type: int = 0):
     """A callable giving the newest K/V row written at (token, layer): a small
     seeded pool, so the host loop does no random drawing while timed."""
     from decode_attention_offloaded_amd import inputs
     g = np.random.default_rng([cfg.seed, 4242])
+    vgen = inputs.random_kv_rows_q4_0 if v_type == 1 else inputs.random_kv_rows
     rows = [(inputs.random_kv_rows(g, 1, cfg.n_head_kv, cfg.head_dim)[0],
-             inputs.random_kv_rows(g, 1, cfg.n_head_kv, cfg.head_dim)[0]) for _ in range(pool * 7)]
+             vgen(g, 1, cfg.n_head_kv, cfg.head_dim)[0]) for _ in range(pool * 7)]
 
     def index(t, l):
         return (t * 7 + l) % len(rows)
@@ -211,23 +220,24 @@ def token_rows(cfg, pool: int = 4):
 
 
 def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budget_bytes=128 << 20, tokens=8,
-                      warmup=3, log=print, n_rows=None, gemv=True, distinct_layers=None):
+                      warmup=3, log=print, n_rows=None, gemv=True, distinct_layers=None, v_type=0):
     """Ordered vs pipelined per-token time for a host-resident stack, arms run
     A/B/B/A (reversed order on the second pass).  Returns a dict for the bench."""
     n_rows = n_rows or cfg.n_ctx
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
-    host = HostKV(n_layers, n_rows, cfg.row_bytes)
+    vrb = inputs.row_bytes_q4_0(cfg.n_head_kv, cfg.head_dim) if v_type == 1 else cfg.row_bytes
+    host = HostKV(n_layers, n_rows, cfg.row_bytes, vrb, v_type)
     host.fill(inputs, cfg, n_rows, distinct=distinct_layers)
     log("host KV: %d layers x %d rows, %.2f GB pinned, filled in %.1f s" %
-        (n_layers, n_rows, 2 * host.k.nbytes / 1e9, time.perf_counter() - t0))
+        (n_layers, n_rows, (host.k.nbytes + host.v.nbytes) / 1e9, time.perf_counter() - t0))
     weights = None
     if gemv:
         gen = torch.Generator(device=dev).manual_seed(cfg.seed)
         m, n = cfg.extra.get("gemv", (5120, 27648))
         weights = [(torch.randn(m, n, dtype=torch.bfloat16, device=dev, generator=gen) * 0.02)
                    for _ in range(n_layers)]
-    rows_fn = token_rows(cfg)
+    rows_fn = token_rows(cfg, v_type=v_type)
     order = list(depths) + list(reversed(depths))
     # One compute stream for every arm, as an engine has one: streams share the
     # process's few hardware queues, and a fresh stream per arm would make the
@@ -253,8 +263,8 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
         del st
         torch.cuda.empty_cache()
     identical = all(torch.equal(a, b) for a, b in zip(outs[depths[0]], outs[depths[-1]]))
-    bytes_token = 2 * n_layers * n_rows * cfg.row_bytes
-    res = {"n_ctx": n_rows, "n_layers": n_layers, "tokens_timed": tokens, "order": order,
+    bytes_token = n_layers * n_rows * (cfg.row_bytes + vrb)
+    res = {"n_ctx": n_rows, "n_layers": n_layers, "tokens_timed": tokens, "order": order, "v_type": v_type,
            "bytes_per_token": bytes_token, "bit_identical": bool(identical), "arms": {}}
     for d in depths:
         ms = float(np.median(times[d]))

@@ -101,7 +101,19 @@ typedef struct kvd_kv_seg {
     int64_t pos0;        /* token position of row 0 */
     int64_t row_stride;  /* bytes between rows; >= row bytes; multiple of 8
                             (head_dim 128) or 4 (head_dim 64); < 2^25 */
+    int64_t v_row_stride;  /* bytes between V rows, or 0 = row_stride; needed when V
+                              rows are q4_0 (shorter); >= V row bytes, multiple of
+                              4, < 2^25 */
 } kvd_kv_seg;
+
+/* Value types of the V cache (K is always q8_0).  q4_0: 18-byte blocks, a
+ * little-endian binary16 scale d, then 16 bytes; value j < 16 = d * (low
+ * nibble of byte j - 8), value 16 + j = d * (high nibble of byte j - 8)
+ * ("F5 — Advanced KV Cache Techniques", M6 (PolyKV), S0: an asymmetric cache
+ * with q8_0 K and q4_0 V, dequantised inside attention; the byte layout is
+ * the reading taken of the named type). */
+#define KVD_TYPE_Q8_0 0
+#define KVD_TYPE_Q4_0 1
 
 typedef struct kvd_attn_args {
     int32_t n_seq;       /* >= 1 */
@@ -122,6 +134,8 @@ typedef struct kvd_attn_args {
     void* workspace;         /* device scratch owned by the caller (256-byte aligned),
                                 or NULL if kvd_attend_workspace_bytes reports 0 */
     size_t workspace_bytes;
+    int32_t v_type;          /* KVD_TYPE_Q8_0 (0) or KVD_TYPE_Q4_0 */
+    int32_t reserved;        /* 0 */
 } kvd_attn_args;
 
 /* Bytes of workspace a call with these arguments needs (validates them too).
@@ -214,7 +228,10 @@ typedef struct kvd_stage_args {
     int64_t cap_rows;     /* capacity the context may grow to; sizes the slots */
     void* ordered_k;      /* device buffer >= n_rows*row_bytes, used when the ring
                              is not engaged (ACQUIRE only; may be NULL for PREFETCH) */
-    void* ordered_v;
+    void* ordered_v;      /* device buffer >= n_rows*v_row_bytes */
+    int64_t v_row_bytes;  /* bytes of one V row, or 0 = row_bytes (a q4_0 V row is
+                             shorter than the q8_0 K row); multiple of 4; the ring
+                             is then (N + 2) * cap_rows * (row_bytes + v_row_bytes) */
 } kvd_stage_args;
 
 typedef struct kvd_slot_view {
@@ -224,6 +241,7 @@ typedef struct kvd_slot_view {
     int64_t row_stride;   /* = row_bytes */
     int32_t pipelined;    /* 1 = ring slot, 0 = ordered buffer */
     int32_t slot;         /* slot index, or -1 */
+    int64_t v_row_stride; /* = v_row_bytes */
 } kvd_slot_view;
 
 /* PREFETCH: returns KVD_OK (prefix copy enqueued on the transfer stream) or

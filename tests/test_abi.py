@@ -155,3 +155,27 @@ def test_merge_and_partial_validate_before_launch():
     a, _ = _args()
     assert L.kvd_attend_decode_partial(ctypes.byref(a), None, None) == kvd.KVD_EINVAL
     assert L.kvd_attend_decode_partial(ctypes.byref(a), ctypes.c_void_p(0x1004), None) == kvd.KVD_EINVAL
+
+
+def test_v_type_and_v_stride_are_validated():
+    L = kvd.lib()
+    a, keep = _args()
+    a.v_type = 7
+    assert L.kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    # q4_0 V rows are 8 x 4 x 18 = 576 bytes: a V stride below that is rejected
+    segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1088, 572))
+    a, _ = _args(segs=segs, v_type=kvd.TYPE_Q4_0)
+    assert L.kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    # q8_0 V with a V stride below the q8_0 row
+    segs2 = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1088, 1000))
+    a, _ = _args(segs=segs2)
+    assert L.kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    # misaligned q4_0 V base
+    segs3 = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20002, 4096, 0, 1088, 576))
+    a, _ = _args(segs=segs3, v_type=kvd.TYPE_Q4_0)
+    assert L.kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+    # a valid q4_0 geometry plans (workspace size is independent of the V type)
+    segs4 = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, 4096, 0, 1088, 576))
+    a4, _ = _args(segs=segs4, v_type=kvd.TYPE_Q4_0)
+    a8, _ = _args()
+    assert kvd.workspace_bytes(a4) == kvd.workspace_bytes(a8)

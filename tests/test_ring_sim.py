@@ -60,25 +60,27 @@ COPY, RECORD, WAIT, CHECK = range(4)
 class Harness:
     """A host-resident stack of layers driven through a simulated ring."""
 
-    def __init__(self, L, depth, budget, n_layers, cap_rows, row_bytes=64, seed=0, fail_after=-1):
+    def __init__(self, L, depth, budget, n_layers, cap_rows, row_bytes=64, seed=0, fail_after=-1, v_row_bytes=0):
         self.L = L
         self.sim = L.sim_new(seed)
         L.sim_configure(self.sim, 1, 0, fail_after)
         self.compute = L.sim_stream_new(self.sim)
         self.ring = L.sim_ring_create(self.sim, depth, budget)
         self.depth, self.n_layers, self.cap, self.rb = depth, n_layers, cap_rows, row_bytes
+        self.vrb_arg = v_row_bytes
+        self.vrb = v_row_bytes or row_bytes
         self.rng = np.random.default_rng(seed)
         self.hk = self.rng.integers(0, 256, (n_layers, cap_rows, row_bytes), dtype=np.uint8)
-        self.hv = self.rng.integers(0, 256, (n_layers, cap_rows, row_bytes), dtype=np.uint8)
+        self.hv = self.rng.integers(0, 256, (n_layers, cap_rows, self.vrb), dtype=np.uint8)
         self.ok = np.zeros(cap_rows * row_bytes, np.uint8)   # "device" ordered buffers (simulated memory is host memory)
-        self.ov = np.zeros(cap_rows * row_bytes, np.uint8)
+        self.ov = np.zeros(cap_rows * self.vrb, np.uint8)
         self.n_checks = 0
 
     def args(self, layer, flags, n_rows, stable=None, cap=None, rb=None):
         rb = rb or self.rb
         return kvd.StageArgs(layer, flags, self.hk[layer].ctypes.data, self.hv[layer].ctypes.data, rb, n_rows,
                              n_rows - 1 if stable is None else stable, cap or self.cap, self.ok.ctypes.data,
-                             self.ov.ctypes.data)
+                             self.ov.ctypes.data, self.vrb_arg)
 
     def stage(self, layer, flags, n_rows, **kw):
         a = self.args(layer, flags, n_rows, **kw)
@@ -87,9 +89,9 @@ class Harness:
         return rc, view
 
     def check(self, layer, view, n_rows):
-        n = n_rows * self.rb
-        self.L.sim_check(self.sim, self.compute, view.k, self.hk[layer].ctypes.data, n, self.n_checks)
-        self.L.sim_check(self.sim, self.compute, view.v, self.hv[layer].ctypes.data, n, self.n_checks + 1)
+        self.L.sim_check(self.sim, self.compute, view.k, self.hk[layer].ctypes.data, n_rows * self.rb, self.n_checks)
+        self.L.sim_check(self.sim, self.compute, view.v, self.hv[layer].ctypes.data, n_rows * self.vrb,
+                         self.n_checks + 1)
         self.n_checks += 2
 
     def step(self, hi=6):
@@ -104,7 +106,7 @@ class Harness:
             self.step(run_hi)
         for l in range(self.n_layers):
             self.hk[l, n_rows - 1] = self.rng.integers(0, 256, self.rb, dtype=np.uint8)
-            self.hv[l, n_rows - 1] = self.rng.integers(0, 256, self.rb, dtype=np.uint8)
+            self.hv[l, n_rows - 1] = self.rng.integers(0, 256, self.vrb, dtype=np.uint8)
             rc, view = self.stage(l, kvd.STAGE_ACQUIRE, n_rows)
             assert rc in (kvd.KVD_OK, kvd.KVD_DECLINED), self.err()
             self.check(l, view, n_rows)
@@ -377,3 +379,25 @@ def test_planner_matches_the_oracle(sim_lib, oracle):
         sim_lib.kvd_ring_release(h.ring, 0, h.compute)
         sim_lib.sim_drain(h.sim)
         h.close()
+
+
+@pytest.mark.parametrize("depth", [1, 2, 4])
+@pytest.mark.parametrize("seed", range(4))
+def test_narrow_v_rows_stage_exactly(sim_lib, depth, seed):
+    """V rows shorter than K rows (a q4_0 V cache): every view holds the host
+    K and V bytes, under random interleavings; the ring is sized
+    (N + 2) x cap x (K row + V row) and the counters count both."""
+    rb, vrb, n, layers = 64, 36, 40, 6
+    need = (depth + 2) * n * (rb + vrb)
+    h = Harness(sim_lib, depth, need, layers, n, row_bytes=rb, seed=seed, v_row_bytes=vrb)
+    for _ in range(3):
+        h.token(n)
+    st = h.stats()
+    assert st["engaged"] == 1 and st["need_bytes"] == need and st["ring_bytes"] == need
+    assert st["n_acquire_ordered"] == 0
+    assert st["bytes_early"] + st["bytes_late"] == 3 * layers * n * (rb + vrb)
+    # one byte less of budget declines, before anything is allocated
+    h2 = Harness(sim_lib, depth, need - 1, layers, n, row_bytes=rb, seed=seed, v_row_bytes=vrb)
+    h2.token(n)
+    st2 = h2.stats()
+    assert st2["declined"] == 1 and st2["n_acquire_ordered"] == layers and st2["bytes_ordered"] == layers * n * (rb + vrb)
