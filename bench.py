@@ -348,6 +348,29 @@ def asymmetric(args, torch, kvd, inputs, link):
     return res
 
 
+def head_split(args, torch, kvd, inputs, link):
+    """131072 rows x 64 layers, about 6.8 GB of device memory spent on residency
+    two ways: 3 of 8 KV heads resident in every layer (the rest staged through
+    a depth-1 ring) against 24 of 64 layers resident (the rest through a
+    depth-1 ring).  Both stage 5/8 of the bytes."""
+    from decode_attention_offloaded_amd import headsplit, stack
+    c = inputs.config(3)
+    L = args.residency_layers
+    peak = max(link.values())
+    hs = headsplit.run_headsplit(torch, kvd, inputs, c, 3, n_layers=L, depths=(0, 1), budget_bytes=1 << 30,
+                                 tokens=args.residency_tokens, warmup=1, log=log, distinct_layers=4)
+    k_layers = L * 3 // 8
+    ls = stack.run_residency(torch, kvd, inputs, c, [("ring+%d" % k_layers, 1, 1 << 30, k_layers),
+                                                     ("ordered+%d" % k_layers, 0, 0, k_layers)],
+                             n_layers=L, tokens=args.residency_tokens, warmup=1, log=log, distinct_layers=4)
+    for arm in hs["arms"].values():
+        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    log("head split 3/8: %s; layer split %d/%d: %s" % (
+        {k: v["ms_per_token"] for k, v in hs["arms"].items()}, k_layers, L,
+        {k: v["ms_per_token"] for k, v in ls["arms"].items()}))
+    return {"head_split": hs, "layer_split": ls, "link_peak_GBps": peak}
+
+
 def long_context(args, torch, kvd, inputs):
     """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
     from decode_attention_offloaded_amd import stack
@@ -451,6 +474,7 @@ def main():
     ap.add_argument("--residency-layers", type=int, default=64)
     ap.add_argument("--residency-tokens", type=int, default=3)
     ap.add_argument("--asym", type=int, default=1, help="run the q8_0 K / q4_0 V legs")
+    ap.add_argument("--headsplit", type=int, default=1, help="run the per-head residency split leg")
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
@@ -489,7 +513,8 @@ def main():
         "device_curve": d["curve"],
         "calibration_copy_bytes": calib,
     }
-    link = link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym) else None
+    link = (link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
+                                 or args.headsplit) else None)
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
     if args.batched:
@@ -500,6 +525,8 @@ def main():
         out["residency"] = residency(args, torch, kvd, inputs, link)
     if args.asym:
         out["asymmetric"] = asymmetric(args, torch, kvd, inputs, link)
+    if args.headsplit:
+        out["head_split"] = head_split(args, torch, kvd, inputs, link)
     if args.long:
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:
