@@ -161,3 +161,53 @@ def test_long_context_sampled_heads(oracle):
         ks, vs = head_slice(k, g, c.n_head_kv, c.head_dim), head_slice(v, g, c.n_head_kv, c.head_dim)
         ref = oracle.attend(q[:, g * G:(g + 1) * G], [[(ks, vs, 0)]], 1, c.head_dim, threads=8)
         check(out[:, g * G:(g + 1) * G], ref)
+
+
+@pytest.mark.parametrize("n,v_type", [(4096, 0), (300, 0), (200000 // 64 * 64, 0), (4096, 1)])
+def test_graph_replays_match_eager(n, v_type):
+    """Decode attention captured in a HIP graph (decode and combine launches,
+    no memset nodes) and replayed several times, with eager work and
+    synchronisations in between: every replay equals the eager call bit for
+    bit, and the partial/merge pair captures the same way."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    rng = np.random.default_rng(n + v_type)
+    k = inputs.random_kv_rows(rng, n, 8, 128)
+    v = inputs.random_kv_rows_q4_0(rng, n, 8, 128) if v_type else inputs.random_kv_rows(rng, n, 8, 128)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    q = torch.from_numpy(inputs.random_q(rng, 1, 40, 128)).cuda()
+    ws = kvd.Workspace()
+    s = torch.cuda.Stream()
+    eager = torch.empty_like(q)
+    with torch.cuda.stream(s):
+        kvd.attend_decode(q, eager, [[(kd, vd, 0)]], 8, workspace=ws, stream=s, v_type=v_type)
+    torch.cuda.synchronize()
+    out = torch.full_like(q, float("nan"))
+    pf = kvd.partial_floats(1, 40, 128)
+    parts = torch.empty(2 * pf, dtype=torch.float32, device="cuda")
+    merged = torch.full_like(q, float("nan"))
+    h = n // 2
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kvd.attend_decode(q, out, [[(kd, vd, 0)]], 8, workspace=ws, stream=s, v_type=v_type)
+        kvd.attend_decode_partial(q, parts[:pf], [[(kd[:h], vd[:h], 0)]], 8, q_pos=[n - 1], workspace=ws,
+                                  stream=s, v_type=v_type)
+        kvd.attend_decode_partial(q, parts[pf:], [[(kd[h:], vd[h:], h)]], 8, q_pos=[n - 1], workspace=ws,
+                                  stream=s, v_type=v_type)
+        kvd.attend_merge(parts, 2, merged, stream=s)
+    first_merged = None
+    for rep in range(4):
+        out.fill_(float("nan"))
+        merged.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        if first_merged is None:
+            first_merged = merged.clone()
+            assert (first_merged - eager).abs().max().item() <= 2e-5
+        assert torch.equal(merged, first_merged), rep
+        # eager work between replays
+        tmp = torch.empty_like(q)
+        kvd.attend_decode(q, tmp, [[(kd, vd, 0)]], 8, v_type=v_type)
+        torch.cuda.synchronize()
