@@ -774,6 +774,14 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             sc[h] = (lane < nv) ? a * A.scale_log2e : -INFINITY;
         }
         {
+            // first tile: start from the score of its first row (always visible)
+            // instead of a wave-wide maximum; the lazy rule below still raises
+            // it if any row passes it by more than kLazyMax
+            if (t == 0) {
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[h])));
+            }
             bool big = false;
 #pragma unroll
             for (int h = 0; h < G; ++h) big |= sc[h] > m[h] + kLazyMax;
@@ -971,10 +979,14 @@ __device__ inline void merge_rows(const Load& load, int n, int lane, float (*so)
             so[lane][4 * j + 3] = w * v[j].w;
         }
         wave_lds_sync();
-        if (lane < 32) {
+        // column sums: lanes 0..31 add rows 0..31, lanes 32..63 rows 32..63, then
+        // the two halves meet (a fixed order)
+        {
+            const int col = lane & 31, r0 = lane & 32;
             float t = 0.f;
 #pragma unroll 16
-            for (int r = 0; r < 64; ++r) t += so[r][lane];
+            for (int r = 0; r < 32; ++r) t += so[r0 + r][col];
+            t += __shfl_xor(t, 32);
             O += t;
         }
         wave_lds_sync();
