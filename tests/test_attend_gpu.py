@@ -211,3 +211,43 @@ def test_graph_replays_match_eager(n, v_type):
         tmp = torch.empty_like(q)
         kvd.attend_decode(q, tmp, [[(kd, vd, 0)]], 8, v_type=v_type)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("v_type", [0, 1])
+def test_more_sequences_than_one_launch(oracle, v_type):
+    """37 sequences: the call is split into launches of 16 sequences; outputs,
+    split partials and the partial-result layout must all line up across
+    launches (also through kvd_attend_decode_partial + kvd_attend_merge)."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    rng = np.random.default_rng(37 + v_type)
+    lens = rng.integers(1, 900, size=37)
+    lens[5] = 3000   # one long sequence: several splits in the middle launch
+    vgen = inputs.random_kv_rows_q4_0 if v_type else inputs.random_kv_rows
+    segs_np = []
+    for n in lens:
+        segs_np.append([(inputs.random_kv_rows(rng, int(n), 2, 64), vgen(rng, int(n), 2, 64), 0)])
+    q = inputs.random_q(rng, 37, 8, 64)
+    qd = torch.from_numpy(q).cuda()
+    dsegs = [[(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), p0) for (k, v, p0) in s] for s in segs_np]
+    out = torch.full_like(qd, float("nan"))
+    kvd.attend_decode(qd, out, dsegs, 2, v_type=v_type)
+    pf = kvd.partial_floats(37, 8, 64)
+    parts = torch.empty(2 * pf + 4, dtype=torch.float32, device="cuda")
+    # two "tiles": the first half of every sequence's rows, then the rest
+    first = [[(k[:max(1, k.shape[0] // 2)], v[:max(1, k.shape[0] // 2)], 0)] for ((k, v, _),) in dsegs]
+    rest = [[(k[max(1, k.shape[0] // 2):], v[max(1, k.shape[0] // 2):], max(1, k.shape[0] // 2))]
+            for ((k, v, _),) in dsegs]
+    qpos = [int(n) - 1 for n in lens]
+    one_row = [i for i, n in enumerate(lens) if n == 1]
+    merged = torch.full_like(qd, float("nan"))
+    if not one_row:
+        kvd.attend_decode_partial(qd, parts[:pf], first, 2, q_pos=qpos, v_type=v_type)
+        kvd.attend_decode_partial(qd, parts[pf:2 * pf], rest, 2, q_pos=qpos, v_type=v_type)
+        kvd.attend_merge(parts[:2 * pf], 2, merged)
+    torch.cuda.synchronize()
+    ref = oracle.attend(q, segs_np, 2, 64, threads=8, v_type=oracle.V_Q4_0 if v_type else oracle.V_Q8_0)
+    got = out.cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-3
+    if not one_row:
+        assert np.abs(merged.cpu().numpy() - ref).max() <= 1e-3
