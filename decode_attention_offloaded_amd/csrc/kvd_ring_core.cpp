@@ -162,14 +162,28 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
                     s, S.layer, a->layer);
     // stream to stream: the copies wait for the release of the slot's previous
     // layer, recorded earlier in host order on the compute stream
-    const size_t bytes[kXferStreams] = {(size_t)rows * (size_t)a->row_bytes, (size_t)rows * (size_t)v_row_bytes_of(a)};
-    void* dst[kXferStreams] = {S.k, S.v};
-    const void* src[kXferStreams] = {a->host_k, a->host_v};
+    // The K and V bytes are shared evenly between the two transfer streams
+    // (one DMA engine each): K on one and V on the other when the rows are
+    // the same size; with narrower V rows the first stream takes the head of
+    // K's bytes and the second the rest of K, then V.
+    const size_t kb = (size_t)rows * (size_t)a->row_bytes;
+    const size_t vb = (size_t)rows * (size_t)v_row_bytes_of(a);
+    size_t split = kb;  // bytes of K on stream 0
+    if (vb < kb) split = ((kb + vb) / 2) & ~(size_t)15;
+    struct Piece {
+        void* dst;
+        const void* src;
+        size_t n;
+    };
+    const Piece pieces[kXferStreams][2] = {
+        {{S.k, a->host_k, split}, {nullptr, nullptr, 0}},
+        {{(uint8_t*)S.k + split, (const uint8_t*)a->host_k + split, kb - split}, {S.v, a->host_v, vb}}};
     for (int x = 0; x < kXferStreams; ++x) {
         if (S.released_once && t_->wait(xfer_[x], S.rel) != 0)
             return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
-        if (bytes[x] > 0 && t_->copy_h2d(dst[x], src[x], bytes[x], xfer_[x]) != 0)
-            return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
+        for (const Piece& pc : pieces[x])
+            if (pc.n > 0 && t_->copy_h2d(pc.dst, pc.src, pc.n, xfer_[x]) != 0)
+                return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
         if (t_->record(S.ready[x], xfer_[x]) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
     }
     S.state = STAGED;

@@ -52,8 +52,9 @@ bool ring_need_bytes(int32_t depth, int64_t cap_rows, int64_t row_bytes, int64_t
 // Bytes of one V row of a stage call (0 in the arguments means = row_bytes).
 inline int64_t v_row_bytes_of(const kvd_stage_args* a) { return a->v_row_bytes ? a->v_row_bytes : a->row_bytes; }
 
-// Transfer streams per ring: K rows go on one, V rows on the other, so two
-// DMA engines copy in parallel (one engine tops out below the host link, and
+// Transfer streams per ring: a delivery's bytes are split evenly between
+// them (K on one and V on the other when the rows are equal), so two DMA
+// engines copy in parallel (one engine tops out below the host link, and
 // engines differ in speed).
 constexpr int kXferStreams = 2;
 
