@@ -98,11 +98,62 @@ def device_resident(args, torch, kvd, inputs):
     if args.curve:
         for n in (16384, 32768, 131072):
             curve[str(n)] = device_curve_point(torch, kvd, inputs, n, stream, ws)
+        for w in (0, 4096):
+            curve["batched_16seq_w%d" % w] = batched_device_point(torch, kvd, inputs, stream, ws, w)
     return {
         "ms_per_step": ms_step, "value": gbs, "us_per_launch": us_launch, "bytes_per_launch": per_launch,
         "layers_per_step": L, "curve": curve,
         "ws": ws, "q": qs[0], "k": ks[0], "v": vs[0],
     }
+
+
+def batched_device_point(torch, kvd, inputs, stream, ws, window):
+    """One call over the 16-sequence batch (lognormal lengths, two segments per
+    sequence: older and newer halves), every row device-resident: GB/s of the
+    visible K/V rows.  8 distinct layer caches cycled."""
+    from decode_attention_offloaded_amd.batched import cfg4_lengths
+    c = inputs.config(4)
+    dev = torch.device("cuda:0")
+    lens = cfg4_lengths(c)
+    reps = 8
+    layers = []
+    for i in range(reps):
+        r = np.random.default_rng([c.seed, 2000 + i])
+        segs = []
+        for n in lens:
+            n = int(n)
+            k = torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev)
+            v = torch.from_numpy(inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)).to(dev)
+            h = n // 2
+            segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
+        q = torch.from_numpy(inputs.random_q(r, len(lens), c.n_head_q, c.head_dim)).to(dev)
+        layers.append((q, segs))
+    out = torch.empty_like(layers[0][0])
+    with torch.cuda.stream(stream):
+        for q, segs in layers:
+            kvd.attend_decode(q, out, segs, c.n_head_kv, window=window, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for q, segs in layers:
+            kvd.attend_decode(q, out, segs, c.n_head_kv, window=window, workspace=ws, stream=stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nrep = 5
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(nrep):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (nrep * reps)
+    vis = sum(min(int(n), window) if window else int(n) for n in lens)
+    b = 2 * vis * c.row_bytes + 2 * len(lens) * c.n_head_q * c.head_dim * 4
+    del layers
+    torch.cuda.empty_cache()
+    return {"us_per_launch": round(us, 3), "visible_rows": vis, "GBps": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def device_curve_point(torch, kvd, inputs, n, stream, ws):
@@ -185,7 +236,7 @@ def pipeline(args, torch, kvd, inputs, link):
     peak = max(link.values())
     log("pinned H2D link: %s GB/s" % link)
     c = inputs.config(2)
-    res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1),
+    res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1, "1x"),
                                   budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log)
     res["link_GBps_by_MiB"] = link
     res["link_peak_GBps"] = peak

@@ -111,13 +111,19 @@ class Stack:
     """Drives one arm (a ring of some depth and budget) over a HostKV."""
 
     def __init__(self, torch, kvd, cfg, host: HostKV, n_rows: int, depth: int, budget_bytes: int,
-                 gemv_weights=None, stream=None, new_rows=None, resident: int = 0):
+                 gemv_weights=None, stream=None, new_rows=None, resident: int = 0, cross_step: bool = False):
         self.torch, self.kvd, self.cfg, self.host = torch, kvd, cfg, host
         self.n_rows, self.depth = n_rows, depth
         dev = torch.device("cuda:0")
         # layers [0, resident) keep their K/V on the device (a resident
         # prefix); the rest are staged through the ring each step
         self.resident = max(0, min(int(resident), host.n_layers))
+        # cross-step look-ahead: after the last layer of a step, the first N
+        # staged layers of the next step are prefetched (their prefix is
+        # stable: a step rewrites only the newest row), so the next step does
+        # not start with an exposed delivery
+        self.cross_step = cross_step
+        self._primed = set()
         self.dev_k = [torch.from_numpy(host.k_rows(l)[:n_rows]).to(dev) for l in range(self.resident)]
         self.dev_v = [torch.from_numpy(host.v_rows(l)[:n_rows]).to(dev) for l in range(self.resident)]
         self.pool_dev = None
@@ -156,7 +162,9 @@ class Stack:
         with torch.cuda.stream(s):
             e0.record(s)
             for l in range(R, min(R + N, L)):
-                self._stage(l, kvd.STAGE_PREFETCH)
+                if l not in self._primed:
+                    self._stage(l, kvd.STAGE_PREFETCH)
+            self._primed = set()
             for l in range(L):
                 if self.gemv is not None:
                     torch.matmul(self.x, self.gemv[l % len(self.gemv)], out=self.y)
@@ -187,6 +195,11 @@ class Stack:
                 self.ring.release(l, stream=s)
                 if l + N < L and N > 0 and l + N >= R + N:
                     self._stage(l + N, kvd.STAGE_PREFETCH)
+            if self.cross_step and N > 0:
+                for l in range(R, min(R + N, L)):
+                    rc, _ = self._stage(l, kvd.STAGE_PREFETCH)
+                    if rc == kvd.KVD_OK:
+                        self._primed.add(l)
             e1.record(s)
         s.synchronize()
         return e0.elapsed_time(e1)
@@ -220,7 +233,8 @@ def token_rows(cfg, pool: int = 4, v_type: int = 0):
 
 
 def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budget_bytes=128 << 20, tokens=8,
-                      warmup=3, log=print, n_rows=None, gemv=True, distinct_layers=None, v_type=0):
+                      warmup=3, log=print, n_rows=None, gemv=True, distinct_layers=None, v_type=0,
+                      cross_step=False):
     """Ordered vs pipelined per-token time for a host-resident stack, arms run
     A/B/B/A (reversed order on the second pass).  Returns a dict for the bench."""
     n_rows = n_rows or cfg.n_ctx
@@ -249,8 +263,10 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         free0 = torch.cuda.mem_get_info(dev)[0]
-        st = Stack(torch, kvd, cfg, host, n_rows, d, budget_bytes, gemv_weights=weights, new_rows=rows_fn,
-                   stream=compute)
+        # an arm is a depth, or "<depth>x" for that depth with cross-step look-ahead
+        depth, cross = int(str(d).rstrip("x")), cross_step or str(d).endswith("x")
+        st = Stack(torch, kvd, cfg, host, n_rows, depth, budget_bytes, gemv_weights=weights, new_rows=rows_fn,
+                   stream=compute, cross_step=cross)
         for t in range(warmup):
             st.token(t)
         free1 = torch.cuda.mem_get_info(dev)[0]
@@ -262,14 +278,15 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
         st.close()
         del st
         torch.cuda.empty_cache()
-    identical = all(torch.equal(a, b) for a, b in zip(outs[depths[0]], outs[depths[-1]]))
+    identical = all(torch.equal(a, b) for d in depths[1:] for a, b in zip(outs[depths[0]], outs[d]))
     bytes_token = n_layers * n_rows * (cfg.row_bytes + vrb)
     res = {"n_ctx": n_rows, "n_layers": n_layers, "tokens_timed": tokens, "order": order, "v_type": v_type,
            "bytes_per_token": bytes_token, "bit_identical": bool(identical), "arms": {}}
     for d in depths:
         ms = float(np.median(times[d]))
         s = stats[d]
-        res["arms"][str(d)] = {"depth": d, "ms_per_token": round(ms, 3), "tokens_per_s": round(1e3 / ms, 3),
+        res["arms"][str(d)] = {"depth": int(str(d).rstrip("x")), "cross_step": cross_step or str(d).endswith("x"),
+                               "ms_per_token": round(ms, 3), "tokens_per_s": round(1e3 / ms, 3),
                                "staged_GBps": round(bytes_token / (ms * 1e-3) / 1e9, 2),
                                "ring_engaged_bytes": s["ring_bytes"] if s["engaged"] else 0,
                                "need_bytes": s["need_bytes"], "declined": s["declined"],

@@ -33,7 +33,10 @@ def run_arm(env, cfg, host, n_rows, depth, budget, tokens, hook=None, after=None
     outs = []
     for t in range(tokens):
         st.token(t)
-        outs.append([o.clone() for o in st.out])
+        # cloned on the stack's stream: the next token's attention writes
+        # `out` on that stream, so a clone on another stream could race it
+        with torch.cuda.stream(st.stream):
+            outs.append([o.clone() for o in st.out])
     s = st.ring.stats()
     st.close()
     return outs, s
@@ -172,3 +175,30 @@ def test_pageable_host_memory_is_rejected(env):
         ring.stage(0, kvd.STAGE_ACQUIRE, a.ctypes.data, a.ctypes.data, 1088, 2, 1, 2, ok.data_ptr(), ok.data_ptr())
     assert e.value.code == kvd.KVD_EINVAL
     ring.close()
+
+
+def test_cross_step_lookahead_is_bit_identical(env):
+    """Prefetching the next step's first layers after the last layer of a step
+    (their prefix is stable) changes nothing in the outputs."""
+    torch, kvd, stack = env
+    cfg = small_cfg()
+    host = stack.HostKV(cfg.n_layers, cfg.n_ctx, cfg.row_bytes)
+    host.fill(inputs, cfg, cfg.n_ctx)
+    ref, _ = run_arm(env, cfg, host, cfg.n_ctx, 0, 0, 3)
+    for depth in (1, 3):
+        st = stack.Stack(torch, kvd, cfg, host, cfg.n_ctx, depth, 1 << 30, new_rows=stack.token_rows(cfg),
+                         cross_step=True)
+        outs = []
+        for t in range(3):
+            st.token(t)
+            with torch.cuda.stream(st.stream):
+                outs.append([o.clone() for o in st.out])
+        s = st.ring.stats()
+        st.close()
+        # steps after the first start from the deliveries issued at the end of the previous step
+        assert s["n_acquire_primed"] == 0 and s["n_acquire_pipelined"] == 3 * cfg.n_layers
+        assert s["n_prefetch"] == 3 * cfg.n_layers + depth   # the last step's look-ahead is never consumed
+        for t in range(3):
+            for l in range(cfg.n_layers):
+                assert torch.equal(outs[t][l], ref[t][l]), (depth, t, l)
+    host.free()
