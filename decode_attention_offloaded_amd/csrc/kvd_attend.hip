@@ -117,10 +117,12 @@ constexpr int kDppRowBcast31 = 0x143;
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
 
+// Lanes of rows outside ROW_MASK read 0.  With a zero `old` and bound_ctrl
+// set, the compiler folds the move into the consuming add or max
+// (v_add_f32_dpp), one instruction per step instead of three.
 template <int CTRL, int ROW_MASK = 0xf>
 __device__ inline float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x),
-                                                                 CTRL, ROW_MASK, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, true));
 }
 
 // Reductions over the 64 lanes of a wave; the result is wave-uniform (read
@@ -655,17 +657,26 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
 
     constexpr int VW = VWin<VT>::W;
+    // Unit 64 i + lane of a 9-dword window tile is row 7 i + (lane + i) / 9,
+    // dword (lane + i) % 9.  With lane = 9 r0 + d0 (d0 < 9), (lane + i) / 9 is
+    // r0 plus a carry (d0 + i >= 9), so each offset is one select and one
+    // three-way add from a per-lane base and a wave-uniform step.
+    const int r0 = (lane * 57) >> 9;  // lane / 9 for lane < 64
+    const int d0 = lane - 9 * r0;
     int32_t voff[9];
     {
-        const int32_t base = win_dword(wave) * 4;
+        const int32_t base = r0 * SG.stride + 4 * d0 + win_dword(wave) * 4;
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-            const int u = i + lane;
-            voff[i] = (7 * i + u / 9) * SG.stride + (u % 9) * 4 + base;
-        }
+        for (int i = 0; i < 9; ++i)
+            voff[i] = base + i * (7 * SG.stride + 4) + (d0 + i >= 9 ? SG.stride - 36 : 0);
     }
     int32_t voffv[VW];
-    {
+    if constexpr (VW == 9) {
+        const int32_t base = r0 * SG.vstride + 4 * d0 + ((VWin<VT>::BB * wave) >> 2) * 4;
+#pragma unroll
+        for (int i = 0; i < 9; ++i)
+            voffv[i] = base + i * (7 * SG.vstride + 4) + (d0 + i >= 9 ? SG.vstride - 36 : 0);
+    } else {
         const int32_t base = ((VWin<VT>::BB * wave) >> 2) * 4;
 #pragma unroll
         for (int i = 0; i < VW; ++i) {

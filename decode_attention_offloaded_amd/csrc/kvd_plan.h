@@ -21,6 +21,7 @@ constexpr int64_t kSliceMaxWork = 4096;  // 64-row tiles x KV heads
 constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
 constexpr int64_t kTargetWaves = 2048;  // 256 CUs x 8 waves: enough sub-tiles to fill the chip
+constexpr int64_t kSliceTargetItems = 512;  // block-sliced workgroups per launch: two per CU
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
 
 struct SegPlan {

@@ -80,9 +80,9 @@ def test_attend_rejects_empty_visible_set():
 def test_workspace_plan():
     a, _ = _args()
     n = kvd.workspace_bytes(a)
-    # 4096 rows x 8 KV heads = 512 tiles of 64 rows, fewer than the 2048 the
-    # planner aims for: one tile per split, 64 splits per head
-    splits = 64
+    # 4096 rows x 8 KV heads = 512 tiles of 64 rows: one workgroup per CU with
+    # two tiles each, i.e. 32 splits per head
+    splits = 32
     expect = 2 * ((splits * 40 * 4 + 255) // 256 * 256) + splits * 40 * 128 * 4
     assert n == expect
     short, _ = _args()
