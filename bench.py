@@ -484,20 +484,32 @@ def cpu_baseline(target_s=15.0):
             "ms_per_layer": round(dt / reps * 1e3, 2)}
 
 
+# sources that decide the decode kernels' HBM traffic: the kernels and the split plan
+TRAFFIC_SOURCES = ("kvd_attend.hip", "kvd_plan.cpp", "kvd_plan.h")
+
+
+def traffic_source_sha():
+    """sha256 over TRAFFIC_SOURCES, in that order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "decode_attention_offloaded_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic():
     """HBM bytes per call from the committed counter summary, or None when the
-    kernel source has changed since the counters were taken."""
-    import hashlib
-    src = os.path.join(ROOT, "decode_attention_offloaded_amd", "csrc", "kvd_attend.hip")
+    kernel or plan source has changed since the counters were taken."""
     prof = os.path.join(ROOT, "profiles", "decode_attention_4096rows_hbm_traffic.md")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = traffic_source_sha()
         fields = {}
         for line in open(prof):
             if ":" in line and line.startswith("    "):
                 k, v = line.strip().split(":", 1)
                 fields[k.strip()] = v.strip()
-        if fields.get("kernel_source_sha256") == sha:
+        if fields.get("source_sha256") == sha:
             return int(fields["traffic_bytes_per_call"])
     except (OSError, KeyError, ValueError):
         pass
@@ -530,8 +542,8 @@ def main():
     ap.add_argument("--long-tokens", type=int, default=3)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(one process drives one GPU; --gpus must be 1).", file=sys.stderr)
         sys.exit(2)
     import torch
     from decode_attention_offloaded_amd import inputs, kvd

@@ -12,6 +12,38 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Tiles (64 rows) per split for the block-sliced kernel, all waves of a
+// workgroup sharing each tile.  A candidate of k tiles gives W workgroups
+// (every visible range cut into splits of k tiles, times the KV heads); the
+// busiest CU then runs ceil(W / CUs) of them, each costing k tiles plus
+// kSliceOverheadTiles of fixed work (start-up, fold, partial write), and 1.6
+// times that when each CU holds a single workgroup (one wave per SIMD hides
+// little latency).  The cheapest candidate wins, the larger on a tie.  On one
+// sequence of 1024 ... 65536 rows x 8 KV heads this picks the measured
+// fastest split or one within 2%.
+int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis) {
+    const int64_t max_k = std::max<int64_t>(1, ceil_div(max_vis, kSubRows));
+    int64_t best_k = 1, best_cost = INT64_MAX;
+    for (int64_t k = 1; k <= max_k;) {
+        const int64_t rows = k * kSubRows;
+        int64_t wgs = 0;
+        for (const SeqPlan& sp : p.seq) wgs += ceil_div(sp.seg[0].n_vis, rows) + ceil_div(sp.seg[1].n_vis, rows);
+        wgs *= n_head_kv;
+        const int64_t per_cu = ceil_div(wgs, kCUs);
+        const int64_t cost = (per_cu == 1 ? 16 : 10) * per_cu * (k + kSliceOverheadTiles);
+        if (cost <= best_cost) {
+            best_cost = cost;
+            best_k = k;
+        } else if (per_cu == 1) {
+            break;  // one workgroup per CU already: larger k only costs more
+        }
+        // every k up to 16, then steps of about 25%
+        const int64_t next = k < 16 ? k + 1 : k + k / 4;
+        k = (k < max_k && next > max_k) ? max_k : next;
+    }
+    return best_k;
+}
+
 }  // namespace
 
 int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
@@ -111,28 +143,24 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
-    // Kernel and waves per workgroup.  Up to kSliceMaxWork tile-heads the
-    // block-sliced kernel (one wave per q8_0 block, D / 32 waves sharing each
-    // tile: short per-wave chains for short contexts); beyond, the lane-per-row
-    // kernel with 8 waves (one workgroup per CU, waves merged in LDS), whose
-    // longer splits keep the merge small.
+    // Kernel and waves per workgroup.  The block-sliced kernel (one wave per
+    // q8_0 block, D / 32 waves sharing each tile) by default; the lane-per-row
+    // kernel (8 waves, one workgroup per CU, waves merged in LDS) for a single
+    // contiguous range of more than kSliceMaxWork tile-heads, where its longer
+    // splits are slightly faster.  Batches of segments balance better over the
+    // block-sliced kernel's smaller workgroups (measured: 73 us against 113 us
+    // for 16 sequences of 1024 ... 20082 rows in two segments each).
     const int64_t work = total_sub * a->n_head_kv;
-    p->kernel = kKernelChoice != 0 ? kKernelChoice : (work <= kSliceMaxWork ? 3 : 1);
+    int ranges = 0;
+    for (const SeqPlan& sp : p->seq) ranges += (sp.seg[0].n_vis > 0) + (sp.seg[1].n_vis > 0);
+    p->kernel = kKernelChoice != 0 ? kKernelChoice : (work > kSliceMaxWork && ranges == 1 ? 1 : 3);
     // only the block-sliced kernel reads q4_0 V or V rows of their own stride
     if (a->v_type != KVD_TYPE_Q8_0 || strides_differ) p->kernel = 3;
     p->waves = p->kernel == 3 ? a->head_dim / 32 : (work >= kTargetWaves) ? 8 : 2;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
         if (p->kernel == 3) {
-            // block-sliced: all waves of a workgroup share each 64-row tile.
-            // About two workgroups per CU; where that would leave a single tile
-            // per workgroup, one workgroup per CU with two tiles instead (the
-            // second tile's loads overlap the first tile's work, and the
-            // combine reads half as many partials).  Measured on 1024 ... 32768
-            // rows x 8 KV heads, this picks the fastest split or one within 1%.
-            int64_t per = std::max<int64_t>(1, ceil_div(work, kSliceTargetItems));
-            if (per == 1 && work > kSliceTargetItems / 2) per = 2;
-            split_rows = (int64_t)kSubRows * per;
+            split_rows = (int64_t)kSubRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis);
         } else {
             const int64_t per_wave = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
             split_rows = (int64_t)kSubRows * p->waves * per_wave;

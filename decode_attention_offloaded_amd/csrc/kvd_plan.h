@@ -11,17 +11,19 @@
 namespace kvd {
 
 constexpr int kSubRows = 64;            // rows per wave sub-tile of the lane-per-row kernel
-// Decode kernel choice: 0 = by problem size (block-sliced for up to
-// kSliceMaxWork tile-heads, lane-per-row beyond); 1 or 3 forces one.
+// Decode kernel choice: 0 = by problem shape (lane-per-row for one visible
+// range of more than kSliceMaxWork tile-heads, block-sliced otherwise); 1 or
+// 3 forces one.
 #ifndef KVD_DECODE_KERNEL
 #define KVD_DECODE_KERNEL 0
 #endif
 constexpr int kKernelChoice = KVD_DECODE_KERNEL;
-constexpr int64_t kSliceMaxWork = 4096;  // 64-row tiles x KV heads
+constexpr int64_t kSliceMaxWork = 8192;  // 64-row tiles x KV heads
 constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
 constexpr int64_t kTargetWaves = 2048;  // 256 CUs x 8 waves: enough sub-tiles to fill the chip
-constexpr int64_t kSliceTargetItems = 512;  // block-sliced workgroups per launch: two per CU
+constexpr int64_t kCUs = 256;              // compute units of the device
+constexpr int64_t kSliceOverheadTiles = 3;  // block-sliced fixed work per workgroup, in tiles
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
 
 struct SegPlan {

@@ -92,6 +92,44 @@ def test_workspace_plan():
     assert kvd.workspace_bytes(forced) == 0
 
 
+def _splits(n_rows_list, seg_rows=None):
+    """Total splits the planner makes, read back from the workspace size
+    (2 x 256-byte-rounded m and l arrays + the o array, 40 heads x 128 dims)."""
+    segs = []
+    for n in n_rows_list:
+        if seg_rows is None:
+            segs.append(kvd.KvSeg(0x10000, 0x20000, n, 0, 1088))
+        else:
+            h = n // 2
+            segs += [kvd.KvSeg(0x10000, 0x20000, h, 0, 1088), kvd.KvSeg(0x10000, 0x20000, n - h, h, 1088)]
+    raw = (kvd.KvSeg * len(segs))(*segs)
+    a, _ = _args(n_seq=len(n_rows_list), n_seg=1 if seg_rows is None else 2)
+    a.segs = raw
+    nb = kvd.workspace_bytes(a)
+    if nb == 0:
+        return 1
+    s = max(0, (nb - 512) // (40 * 130 * 4))
+    while 2 * ((s * 160 + 255) // 256 * 256) + s * 40 * 128 * 4 < nb:
+        s += 1
+    assert 2 * ((s * 160 + 255) // 256 * 256) + s * 40 * 128 * 4 == nb
+    return s
+
+
+@pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (16384, 64), (32768, 64),
+                                      (65536, 64), (131072, 32)])
+def test_split_plan_single_sequence(n, splits):
+    """Splits per KV head on one sequence of n rows x 8 KV heads (the measured
+    fastest: 64-row splits up to 2048 rows, then about two workgroups per CU;
+    131072 rows go to the lane-per-row kernel, 4096 rows per workgroup)."""
+    assert _splits([n]) == splits
+
+
+def test_split_plan_batch():
+    """16 sequences in two segments each: 1024-row splits, so 92 in all."""
+    lens = [1024, 1024, 1862, 1990, 2813, 3712, 3769, 4264, 5376, 5801, 6363, 6588, 7292, 8678, 9634, 10041]
+    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 1024) + -(-(n - n // 2) // 1024) for n in lens) == 92
+
+
 def test_workspace_too_small_is_rejected():
     a, _ = _args()
     a.workspace = 0x100000
