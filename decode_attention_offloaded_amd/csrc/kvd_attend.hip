@@ -728,16 +728,12 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             uint32_t w[9];
 #pragma unroll
             for (int j = 0; j < 9; ++j) w[j] = rp[j];
-            // query chunks of 4 dims x G heads from LDS, one chunk ahead; the
-            // empty asm statements keep the reads from being hoisted (and the
-            // query from occupying more than two chunks of registers)
-            float4 qc[G];
-            {
-                int off = 0;
-                asm volatile("" : "+v"(off));
-#pragma unroll
-                for (int h = 0; h < G; ++h) qc[h] = *(const float4*)&sq[h * 32 + off];
-            }
+            // query chunks of 4 dims x G heads from LDS, each read just before
+            // its FMAs; the empty asm statements keep the reads from being
+            // hoisted, so the query holds one chunk of registers.  (G = 5: 125
+            // VGPRs instead of 140 when reading one chunk ahead, so four
+            // workgroups fit a CU instead of three, and their waves hide the
+            // LDS latency that the read-ahead used to.)
             float dot[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) dot[h] = 0.f;
@@ -745,12 +741,12 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             for (int c = 0; c < 8; ++c) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
-                float4 qn[G];
-                if (c + 1 < 8) {
-                    int off = 4 * (c + 1);
+                float4 qc[G];
+                {
+                    int off = 4 * c;
                     asm volatile("" : "+v"(off));
 #pragma unroll
-                    for (int h = 0; h < G; ++h) qn[h] = *(const float4*)&sq[h * 32 + off];
+                    for (int h = 0; h < G; ++h) qc[h] = *(const float4*)&sq[h * 32 + off];
                 }
                 const uint32_t x = ODD ? w[c + 1] : __builtin_amdgcn_alignbyte(w[c + 1], w[c], 2);
                 const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
@@ -760,10 +756,6 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
                     dot[h] = fmaf(qc[h].y, k1, dot[h]);
                     dot[h] = fmaf(qc[h].z, k2, dot[h]);
                     dot[h] = fmaf(qc[h].w, k3, dot[h]);
-                }
-                if (c + 1 < 8) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) qc[h] = qn[h];
                 }
             }
             const float dk = ODD ? half_hi(w[0]) : half_lo(w[0]);
