@@ -163,6 +163,28 @@ def test_long_context_sampled_heads(oracle):
         check(out[:, g * G:(g + 1) * G], ref)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g_size", [1, 2, 4, 8])
+def test_long_range_every_group_size(oracle, d, g_size):
+    """One range of 65600 rows x 8 KV heads (8200 tile-heads, just past the
+    block-sliced kernel's limit for a single range, ragged last tile) runs on
+    the lane-per-row kernel; the same rows in two segments run on the
+    block-sliced kernel.  Sampled KV heads of both against the oracle, for
+    every GQA group size the kernels are built for."""
+    n, hkv = 65600, 8
+    hq = hkv * g_size
+    rng, k, v = make_cache(7000 + d + g_size, n, hkv, d)
+    q = inputs.random_q(rng, 1, hq, d)
+    one = gpu_attend(q, [[(k, v, 0)]], hkv)
+    h = n // 3
+    two = gpu_attend(q, [[(k[:h], v[:h], 0), (k[h:], v[h:], h)]], hkv)
+    for g in (1, hkv - 2):
+        ks, vs = head_slice(k, g, hkv, d), head_slice(v, g, hkv, d)
+        ref = oracle.attend(q[:, g * g_size:(g + 1) * g_size], [[(ks, vs, 0)]], 1, d, threads=8)
+        check(one[:, g * g_size:(g + 1) * g_size], ref)
+        check(two[:, g * g_size:(g + 1) * g_size], ref)
+
+
 @pytest.mark.parametrize("n,v_type", [(4096, 0), (300, 0), (200000 // 64 * 64, 0), (4096, 1)])
 def test_graph_replays_match_eager(n, v_type):
     """Decode attention captured in a HIP graph (decode and combine launches,
