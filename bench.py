@@ -489,12 +489,17 @@ TRAFFIC_SOURCES = ("kvd_attend.hip", "kvd_plan.cpp", "kvd_plan.h")
 
 
 def traffic_source_sha():
-    """sha256 over TRAFFIC_SOURCES, in that order."""
+    """sha256 over the code of TRAFFIC_SOURCES, in that order, with comments
+    and whitespace removed (an edit of a comment does not change the kernels)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, "decode_attention_offloaded_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_attention_offloaded_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

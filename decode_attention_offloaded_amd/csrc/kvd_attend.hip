@@ -9,9 +9,17 @@
 // online-softmax rule (same page, M4 step 6 and W4: partial attention results
 // merged by their running maxima and sums).
 //
-// Shape of the work.  One workgroup = NW waves (2, or 8 for long contexts) =
-// one (sequence, KV head, row range) split.  Each wave walks 64-row sub-tiles
-// of its split:
+// Shape of the work.  A split = one (sequence, KV head, row range) = one
+// workgroup; two kernels cover it, chosen by the split plan (kvd_plan.cpp):
+//  * slice_kernel (the default): D / 32 waves, wave w owning q8_0 block w
+//    (dims 32w .. 32w + 31) of every row.  All waves walk the same 64-row
+//    tiles: each loads a 36-byte window around its block (K and V, one tile
+//    ahead in registers), scores its block's 32 dims for all G query heads
+//    (one lane per row, the query from LDS), the D / 32 block partials meet
+//    in LDS at one barrier per tile, every wave runs the same online softmax,
+//    and wave w accumulates the values of its 32 dims.
+//  * decode_kernel (one long contiguous range): NW waves (8: one workgroup
+//    per CU), each walking its own 64-row sub-tiles over all D dims:
 //   1. the sub-tile's K and V chunks (34-byte q8_0 blocks, head g only) are
 //      fetched with coalesced buffer loads (8-byte units for head_dim 128,
 //      4-byte for 64) into registers one sub-tile ahead, then copied into the
@@ -24,13 +32,14 @@
 //      the running sums only when a maximum grows, p = exp2(s - m) per lane;
 //   4. values: 16 dimensions per lane (head_dim/16 lanes per row); each V
 //      code is converted once and used for all G query heads; p * d is folded
-//      per (row, block) so the inner loop is one FMA per head per value.
-// The waves' states merge in LDS; a split with siblings writes an
-// unnormalised partial (m, l, o) to the workspace and a second, small launch
-// merges the partials of each (sequence, KV head) in split order, so the
-// result depends only on the split plan.  (Merging inside the first launch
-// would need device-scope release/acquire between workgroups, which on this
-// chip writes back and invalidates the whole L2 of an XCD per workgroup.)
+//      per (row, block) so the inner loop is one FMA per head per value;
+//   and the waves' states merge in LDS.
+// A split with siblings writes an unnormalised partial (m, l, o) to the
+// workspace and a second, small launch merges the partials of each
+// (sequence, query head) in split order, so the result depends only on the
+// split plan.  (Merging inside the first launch would need device-scope
+// release/acquire between workgroups, which on this chip writes back and
+// invalidates the whole L2 of an XCD per workgroup.)
 // No MFMA: one query row per head is not a dense contraction.
 #include <hip/hip_runtime.h>
 #include <math.h>
