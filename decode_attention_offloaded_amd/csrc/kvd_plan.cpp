@@ -65,6 +65,7 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     if (!a->q || !a->segs) return fail(KVD_EINVAL, "q and segs must not be NULL");
     if ((uintptr_t)a->q % 16) return fail(KVD_EINVAL, "q must be 16-byte aligned");
 
+    if (a->reserved != 0) return fail(KVD_EINVAL, "reserved field must be 0");
     if (a->v_type != KVD_TYPE_Q8_0 && a->v_type != KVD_TYPE_Q4_0)
         return fail(KVD_EINVAL, "v_type %d must be KVD_TYPE_Q8_0 or KVD_TYPE_Q4_0", a->v_type);
     const int D = a->head_dim;

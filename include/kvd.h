@@ -87,7 +87,7 @@ const char* kvd_version(void);
  * results merged by the online-softmax rule).
  *
  * Work is split over (sequence, KV head, row range); each split keeps an
- * online-softmax partial and the partials of one (sequence, KV head) are
+ * online-softmax partial and the partials of one (sequence, query head) are
  * merged in a fixed order by a second launch on the same stream.  The split
  * plan depends only on the shapes (never on pointers, timing or the ring), so
  * two calls with equal shapes and equal input bytes give bit-identical
@@ -95,7 +95,8 @@ const char* kvd_version(void);
  */
 typedef struct kvd_kv_seg {
     const void* k;       /* device: K row 0 of this segment (q8_0 rows) */
-    const void* v;       /* device: V row 0 (same geometry as k) */
+    const void* v;       /* device: V row 0 (the same rows as k: q8_0 like k, or
+                            q4_0 when v_type is KVD_TYPE_Q4_0) */
     int64_t n_rows;      /* rows in the segment, 0 <= n_rows < 2^31; rows
                             [0, n_rows) must be readable */
     int64_t pos0;        /* token position of row 0 */
@@ -135,7 +136,7 @@ typedef struct kvd_attn_args {
                                 or NULL if kvd_attend_workspace_bytes reports 0 */
     size_t workspace_bytes;
     int32_t v_type;          /* KVD_TYPE_Q8_0 (0) or KVD_TYPE_Q4_0 */
-    int32_t reserved;        /* 0 */
+    int32_t reserved;        /* must be 0 (KVD_EINVAL otherwise) */
 } kvd_attn_args;
 
 /* Bytes of workspace a call with these arguments needs (validates them too).
@@ -181,25 +182,26 @@ int kvd_attend_merge(const float* partials, int32_t n_part, int32_t n_seq, int32
  * A ring stages one attention layer's K and V from pinned host memory into
  * device slots ahead of use ([R4] What it does 2 and 3).  It has depth N
  * (look-ahead in layers) and N + 2 slots; each slot holds cap_rows rows of K
- * and of V.  Its device cost is (N + 2) * 2 * cap_rows * row_bytes, checked
- * against budget_bytes before anything is allocated, on every stage call;
- * once over budget the ring declines for good ([R4] Device memory: checked
- * before allocating, latched).  Slots, events and the transfer stream are
- * created on the first stage call that engages the ring and freed by
- * kvd_ring_destroy ([R4] Device memory: the transport is lazy).  Depth 0 is
- * the ordered path exactly: it never allocates anything.
+ * and of V.  Its device cost is (N + 2) * cap_rows * (row_bytes +
+ * v_row_bytes), checked against budget_bytes before anything is allocated,
+ * on every stage call; once over budget the ring declines for good ([R4]
+ * Device memory: checked before allocating, latched).  Slots, events and the
+ * ring's two transfer streams (a delivery's bytes split evenly between them,
+ * one DMA engine each) are created on the first stage call that engages the
+ * ring and freed by kvd_ring_destroy ([R4] Device memory: the transport is
+ * lazy).  Depth 0 is the ordered path exactly: it never allocates anything.
  *
  * Per layer l of a decode step the caller does:
  *   1. write the newest row(s) of layer l into the pinned host K/V;
  *   2. kvd_ring_stage_layer(flags = ACQUIRE, layer l) -> a view of l's K/V in
  *      device memory, ordered on `compute` (the ordered path copies the whole
  *      layer there; the pipelined path copies only the tail rows there and
- *      waits for the prefix copied earlier on the transfer stream);
+ *      waits for the prefix copied earlier on the transfer streams);
  *   3. enqueue attention (kvd_attend_decode) on the view, on `compute`;
  *   4. kvd_ring_release(layer l, compute): the slot is free once `compute`
  *      passes this point;
  *   5. kvd_ring_stage_layer(flags = PREFETCH, layer l + N): start copying the
- *      stable prefix of layer l + N on the transfer stream.  It waits,
+ *      stable prefix of layer l + N on the transfer streams.  They wait,
  *      stream to stream, for the release of the slot it reuses ([R4] What it
  *      does 3: issued after the consumer is enqueued, never a host sync).
  * ACQUIRE of a layer that was not prefetched (e.g. the first N layers of a
@@ -220,7 +222,8 @@ typedef struct kvd_stage_args {
     int32_t flags;        /* KVD_STAGE_PREFETCH or KVD_STAGE_ACQUIRE */
     const void* host_k;   /* PINNED host: K rows [cap_rows][row_bytes] of this layer */
     const void* host_v;   /* PINNED host: V rows, same geometry */
-    int64_t row_bytes;    /* bytes of one K row (= one V row); multiple of 8 */
+    int64_t row_bytes;    /* bytes of one K row (= one V row unless v_row_bytes
+                             says otherwise); multiple of 4, <= 2^24 */
     int64_t n_rows;       /* rows to deliver: [0, n_rows); 1 <= n_rows <= cap_rows */
     int64_t stable_rows;  /* rows [0, stable_rows) are not written again before
                              this layer's release ([R4] What it does 1: the stable
@@ -244,7 +247,7 @@ typedef struct kvd_slot_view {
     int64_t v_row_stride; /* = v_row_bytes */
 } kvd_slot_view;
 
-/* PREFETCH: returns KVD_OK (prefix copy enqueued on the transfer stream) or
+/* PREFETCH: returns KVD_OK (prefix copy enqueued on the transfer streams) or
  *   KVD_DECLINED (ring not engaged: nothing done).  `out` may be NULL.
  * ACQUIRE: returns KVD_OK with a slot view (pipelined) or KVD_DECLINED with a
  *   view of ordered_k/ordered_v after enqueuing the whole-layer copy on
@@ -273,7 +276,7 @@ typedef struct kvd_ring_stats {
     int32_t device;           /* HIP device the ring is bound to, or -1 */
     int32_t reserved;
     int64_t budget_bytes;
-    int64_t need_bytes;       /* size of the last plan: (N+2)*2*cap_rows*row_bytes */
+    int64_t need_bytes;       /* size of the last plan: (N+2)*cap_rows*(row_bytes+v_row_bytes) */
     int64_t ring_bytes;       /* device bytes held by slots now */
     int64_t slot_rows;        /* rows per slot */
     int64_t n_prefetch;       /* prefix deliveries issued ahead */
@@ -288,8 +291,8 @@ typedef struct kvd_ring_stats {
 /* Copy the counters into *out (out_size must be >= sizeof(kvd_ring_stats)). */
 int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, size_t out_size);
 
-/* Wait for the transfer stream and every slot's release, then free slots,
- * events and the transfer stream.  NULL is a no-op. */
+/* Wait for the transfer streams and every slot's release, then free slots,
+ * events and the transfer streams.  NULL is a no-op. */
 void kvd_ring_destroy(kvd_ring* ring);
 
 /* Tile size for tile-streamed attention through a ring of this depth and

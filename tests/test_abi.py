@@ -45,7 +45,7 @@ def _args(**kw):
 
 @pytest.mark.parametrize("field,value", [("head_dim", 96), ("head_dim", 256), ("n_head_q", 41), ("n_head_q", 72),
                                          ("n_seg", 3), ("n_seq", 0), ("window", -1), ("split_rows", 100),
-                                         ("q", None), ("out", None)])
+                                         ("q", None), ("out", None), ("reserved", 1)])
 def test_attend_rejects_bad_arguments(field, value):
     a, keep = _args(**{field: value})
     assert kvd.lib().kvd_attend_decode(ctypes.byref(a), None) == kvd.KVD_EINVAL
