@@ -207,7 +207,12 @@ def workspace_bytes(args: AttnArgs) -> int:
 
 
 class Workspace:
-    """Per-device scratch for split partials, grown on demand and reused."""
+    """Per-device scratch for split partials, grown on demand and reused.
+
+    Calls that share a workspace must be ordered (one stream, or streams
+    ordered by events): they write the same partials.  Growing it waits for
+    the device first, so no launch still in flight uses the buffer it drops.
+    """
 
     def __init__(self):
         self._buf = {}
@@ -219,6 +224,9 @@ class Workspace:
         key = torch.device(device).index
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
+            if buf is not None:
+                torch.cuda.synchronize(device)
+                nbytes = max(nbytes, 2 * buf.numel())
             buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             self._buf[key] = buf
         return buf
@@ -229,7 +237,10 @@ _default_ws = Workspace()
 
 def attend_decode(q, out, segs, n_head_kv: int, window: int = 0, scale: Optional[float] = None, q_pos=None,
                   split_rows: int = 0, stream=None, workspace: Optional[Workspace] = None, v_type: int = TYPE_Q8_0):
-    """Enqueue decode attention on ``stream`` (default: torch's current stream)."""
+    """Enqueue decode attention on ``stream`` (default: torch's current stream).
+
+    ``workspace`` holds the split partials (default: one shared by every call
+    that passes none); calls that share one must be ordered on the device."""
     import torch
     if not (q.is_cuda and out.is_cuda) or q.dtype != torch.float32 or out.dtype != torch.float32:
         raise ValueError("q and out must be float32 CUDA tensors")
