@@ -211,11 +211,14 @@ class Workspace:
 
     Calls that share a workspace must be ordered (one stream, or streams
     ordered by events): they write the same partials.  Growing it waits for
-    the device first, so no launch still in flight uses the buffer it drops.
+    the device first, so no launch still in flight uses the buffer it drops;
+    under graph capture (where waiting is not allowed) the old buffer is kept
+    instead.
     """
 
     def __init__(self):
         self._buf = {}
+        self._kept = []
 
     def get(self, nbytes: int, device):
         import torch
@@ -225,7 +228,10 @@ class Workspace:
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
             if buf is not None:
-                torch.cuda.synchronize(device)
+                if torch.cuda.is_current_stream_capturing():
+                    self._kept.append(buf)
+                else:
+                    torch.cuda.synchronize(device)
                 nbytes = max(nbytes, 2 * buf.numel())
             buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             self._buf[key] = buf
