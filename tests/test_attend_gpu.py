@@ -235,6 +235,53 @@ def test_graph_replays_match_eager(n, v_type):
         torch.cuda.synchronize()
 
 
+def test_workspace_grows_eagerly_and_under_capture():
+    """A workspace sized by a short call grows for larger ones: between eager
+    calls (after a device wait: 1024 rows, then 16384) and during graph
+    capture (keeping the old buffer: 16384 rows with 64 query heads, more
+    partials per split).  Outputs equal those of calls with a fresh
+    workspace of their own, and the captured call replays to the same bytes."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    rng = np.random.default_rng(4321)
+
+    def cache(n, hq):
+        kd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
+        vd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
+        return torch.from_numpy(inputs.random_q(rng, 1, hq, 128)).cuda(), [[(kd, vd, 0)]]
+
+    calls = [cache(1024, 40), cache(16384, 40), cache(16384, 64)]
+    refs = []
+    for q, segs in calls:
+        r = torch.empty_like(q)
+        kvd.attend_decode(q, r, segs, 8, workspace=kvd.Workspace())
+        refs.append(r)
+    torch.cuda.synchronize()
+    ws = kvd.Workspace()
+    s = torch.cuda.Stream()
+    sizes = []
+    with torch.cuda.stream(s):
+        for (q, segs), ref in zip(calls[:2], refs[:2]):   # grows between eager calls
+            out = torch.empty_like(q)
+            kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s)
+            s.synchronize()
+            assert torch.equal(out, ref)
+            sizes.append(ws._buf[torch.cuda.current_device()].numel())
+    q, segs = calls[2]
+    out = torch.full_like(q, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):                     # grows during capture
+        kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s)
+    sizes.append(ws._buf[torch.cuda.current_device()].numel())
+    assert sizes[0] < sizes[1] < sizes[2], sizes
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, refs[2]), rep
+
+
 @pytest.mark.parametrize("v_type", [0, 1])
 def test_more_sequences_than_one_launch(oracle, v_type):
     """37 sequences: the call is split into launches of 16 sequences; outputs,
