@@ -437,6 +437,32 @@ def long_context(args, torch, kvd, inputs):
     return out
 
 
+def hbm_stream_ceiling(torch, gib=4, reps=7):
+    """GB/s of plain streaming on this device: torch's elementwise negation of
+    a `gib` GiB float32 tensor into another (reads and writes every byte once;
+    of torch's kernels it streams fastest here: its reductions reach ~4 TB/s),
+    median of `reps` runs.  A measured ceiling beside the 8 TB/s spec."""
+    n = gib << 30
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(x, out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del x, y
+    torch.cuda.empty_cache()
+    ms = sorted(times)[len(times) // 2]
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel": "torch.neg, %d GiB float32 read + %d GiB written, median of %d" % (gib, gib, reps)}
+
+
 def calibration_copy(torch, mib=256):
     """A plain device-to-device copy of known size: the reference that hardware
     fetch/write counters are scaled by when the traffic of the decode kernel is
@@ -503,6 +529,56 @@ def traffic_source_sha():
     return h.hexdigest()
 
 
+def cpu_baseline_extra(target_s=10.0):
+    """The oracle on more of the workloads (opt-in, --cpu-extra): the 4096-row
+    layer on one core; one layer at 16384 and at 131072 rows and the
+    16-sequence batch (full and 4096-row window) on every core."""
+    import oracle
+    from decode_attention_offloaded_amd import inputs
+    from decode_attention_offloaded_amd.batched import cfg4_lengths
+    cores = len(os.sched_getaffinity(0))
+    res = {}
+
+    def timed(name, q, segs, hkv, d, threads, window, b):
+        t0 = time.perf_counter()
+        oracle.attend(q, segs, hkv, d, threads=threads, window=window)
+        one = time.perf_counter() - t0
+        reps = max(1, int(target_s / max(one, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.attend(q, segs, hkv, d, threads=threads, window=window)
+        dt = (time.perf_counter() - t0) / reps
+        res[name] = {"ms_per_layer": round(dt * 1e3, 2), "GBps": round(b / dt / 1e9, 4), "threads": threads,
+                     "calls": reps}
+
+    for cfg, n, threads in ((1, 4096, 1), (2, 16384, cores), (3, 131072, cores)):
+        c = inputs.config(cfg)
+        r = c.layer_rng(0)
+        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        q = inputs.random_q(r, 1, c.n_head_q, c.head_dim)
+        timed("%d rows, %d thread%s" % (n, threads, "s" if threads > 1 else ""), q, [[(k, v, 0)]], c.n_head_kv,
+              c.head_dim, threads, 0, algorithmic_bytes(n, c.n_head_kv, c.head_dim, c.n_head_q))
+    c = inputs.config(4)
+    r = c.layer_rng(0)
+    lens = [int(x) for x in cfg4_lengths(c)]
+    segs, nb_full, nb_win = [], 0, 0
+    for n in lens:
+        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        h = n // 2
+        segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
+        nb_full += 2 * n * c.row_bytes
+        nb_win += 2 * min(n, 4096) * c.row_bytes
+    q = inputs.random_q(r, len(lens), c.n_head_q, c.head_dim)
+    qb = 2 * len(lens) * c.n_head_q * c.head_dim * 4
+    timed("16 sequences, full attention, %d threads" % cores, q, segs, c.n_head_kv, c.head_dim, cores, 0,
+          nb_full + qb)
+    timed("16 sequences, 4096-row window, %d threads" % cores, q, segs, c.n_head_kv, c.head_dim, cores, 4096,
+          nb_win + qb)
+    return {"cores": cores, "kind": "oracle", "workloads": res}
+
+
 def measured_traffic():
     """HBM bytes per call from the committed counter summary, or None when the
     kernel or plan source has changed since the counters were taken."""
@@ -545,6 +621,8 @@ def main():
     ap.add_argument("--headsplit", type=int, default=1, help="run the per-head residency split leg")
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
     ap.add_argument("--long-tokens", type=int, default=3)
+    ap.add_argument("--cpu-extra", type=int, default=0,
+                    help="also time the oracle single-threaded and on the 16384/131072-row and batched layers")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -579,8 +657,10 @@ def main():
                      "kernel": "slice_kernel<128,5> + combine_kernel<128> (one call)",
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
+        "hbm_stream_ceiling": hbm_stream_ceiling(torch),
         "calibration_copy_bytes": calib,
     }
+    log("streaming ceiling: %s" % out["hbm_stream_ceiling"])
     link = (link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
                                  or args.headsplit) else None)
     if args.pipeline:
@@ -599,6 +679,8 @@ def main():
         out["long_context"] = long_context(args, torch, kvd, inputs)
     if args.cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+    if args.cpu_extra:
+        out["cpu_baseline_extra"] = cpu_baseline_extra()
     print(json.dumps(out), flush=True)
 
 
