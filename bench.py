@@ -200,9 +200,9 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
 
 def link_peak(torch):
     """Pinned host -> device copy bandwidth (GB/s): one copy on one stream at
-    several sizes, and two equal copies on two streams at once (the ring's
-    configuration: K and V on their own DMA engines).  The peak is the best
-    plateau."""
+    1 MiB ... 1 GiB, and two equal copies on two streams at once (the ring's
+    configuration: K and V on their own DMA engines); median of 10 timed runs
+    (5 at 1 GiB) after one untimed.  The peak is the best plateau."""
     dev = torch.device("cuda:0")
     res = {}
     s0, s1 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
@@ -211,7 +211,7 @@ def link_peak(torch):
         hs = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in streams]
         ds = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in streams]
         times = []
-        for _ in range(6):
+        for _ in range(11 if n <= (256 << 20) else 6):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for s, h, d in zip(streams, hs, ds):
@@ -222,7 +222,7 @@ def link_peak(torch):
         t = float(np.median(times[1:]))
         return round(n * len(streams) / t / 1e9, 2)
 
-    for mib in (1, 16, 64, 256):
+    for mib in (1, 16, 64, 256, 1024):
         res["1x%dMiB" % mib] = run(mib << 20, [s0])
     for mib in (16, 64, 256):
         res["2x%dMiB" % mib] = run(mib << 20, [s0, s1])
