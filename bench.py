@@ -463,6 +463,42 @@ def hbm_stream_ceiling(torch, gib=4, reps=7):
             "kernel": "torch.neg, %d GiB float32 read + %d GiB written, median of %d" % (gib, gib, reps)}
 
 
+def stream_same_bytes(torch, nbytes, reps=20):
+    """The rate a single streaming launch of one decode call's size reaches
+    here: torch's elementwise negation reading nbytes / 2 and writing nbytes / 2,
+    graph-replayed over distinct buffers (at least 2.5 GB in all, as the decode
+    calls cycle distinct layers), so launch and first-byte latency weigh as
+    they do for a call.  Returns {"bytes", "us", "GBps", "frac_of_peak"}."""
+    n = nbytes // 8
+    count = max(4, min(64, int(2.5e9 // nbytes)))
+    xs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(count)]
+    ys = [torch.empty_like(x) for x in xs]
+    s = torch.cuda.Stream(device=torch.device("cuda:0"))
+    with torch.cuda.stream(s):
+        for x, y in zip(xs, ys):
+            torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for x, y in zip(xs, ys):
+            torch.neg(x, out=y)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * count)
+    del xs, ys, g
+    torch.cuda.empty_cache()
+    moved = 8 * n
+    gbs = moved / (us * 1e-6) / 1e9
+    return {"bytes": moved, "us": round(us, 3), "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def calibration_copy(torch, mib=256):
     """A plain device-to-device copy of known size: the reference that hardware
     fetch/write counters are scaled by when the traffic of the decode kernel is
@@ -660,6 +696,13 @@ def main():
         "hbm_stream_ceiling": hbm_stream_ceiling(torch),
         "calibration_copy_bytes": calib,
     }
+    if args.curve:
+        # what one streaming launch moving a call's algorithmic bytes reaches
+        c1 = inputs.config(1)
+        same = {}
+        for n in (4096, 16384, 32768, 131072):
+            same[str(n)] = stream_same_bytes(torch, algorithmic_bytes(n, c1.n_head_kv, c1.head_dim, c1.n_head_q))
+        out["hbm_stream_ceiling"]["same_bytes_as_call"] = same
     log("streaming ceiling: %s" % out["hbm_stream_ceiling"])
     link = (link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
                                  or args.headsplit) else None)
