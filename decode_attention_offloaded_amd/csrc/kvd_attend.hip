@@ -10,30 +10,13 @@
 // merged by their running maxima and sums).
 //
 // Shape of the work.  A split = one (sequence, KV head, row range) = one
-// workgroup; two kernels cover it, chosen by the split plan (kvd_plan.cpp):
-//  * slice_kernel (the default): D / 32 waves, wave w owning q8_0 block w
-//    (dims 32w .. 32w + 31) of every row.  All waves walk the same 64-row
-//    tiles: each loads a 36-byte window around its block (K and V, one tile
-//    ahead in registers), scores its block's 32 dims for all G query heads
-//    (one lane per row, the query from LDS), the D / 32 block partials meet
-//    in LDS at one barrier per tile, every wave runs the same online softmax,
-//    and wave w accumulates the values of its 32 dims.
-//  * decode_kernel (one long contiguous range): NW waves (8: one workgroup
-//    per CU), each walking its own 64-row sub-tiles over all D dims:
-//   1. the sub-tile's K and V chunks (34-byte q8_0 blocks, head g only) are
-//      fetched with coalesced buffer loads (8-byte units for head_dim 128,
-//      4-byte for 64) into registers one sub-tile ahead, then copied into the
-//      wave's own LDS tile in row order;
-//   2. scores: one lane per row; the row's K bytes are realigned from LDS
-//      (v_alignbyte), each signed code is converted with one SDWA convert and
-//      multiplied by the G query rows held in SGPRs (scalar loads), the block
-//      scale is applied once per 32 codes;
-//   3. online softmax in the exp2 domain: wave maxima by shuffles, rescale of
-//      the running sums only when a maximum grows, p = exp2(s - m) per lane;
-//   4. values: 16 dimensions per lane (head_dim/16 lanes per row); each V
-//      code is converted once and used for all G query heads; p * d is folded
-//      per (row, block) so the inner loop is one FMA per head per value;
-//   and the waves' states merge in LDS.
+// workgroup of D / 32 waves, wave w owning q8_0 block w (dims 32w .. 32w + 31)
+// of every row.  All waves walk the same 64-row tiles: each loads a 36-byte
+// window around its block (K and V, one tile ahead in registers), scores its
+// block's 32 dims for all G query heads (one lane per row; the query chunks
+// from LDS or, once several workgroups share a CU, from SGPRs), the D / 32
+// block partials meet in LDS at one barrier per tile, every wave runs the same
+// online softmax, and wave w accumulates the values of its 32 dims.
 // A split with siblings writes an unnormalised partial (m, l, o) to the
 // workspace and a second, small launch merges the partials of each
 // (sequence, query head) in split order, so the result depends only on the
@@ -46,7 +29,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <type_traits>
 
 #include "kvd_internal.h"
 #include "kvd_plan.h"
@@ -54,7 +36,6 @@
 namespace kvd {
 namespace {
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // Constant address space: loads through it are scalar (s_load) when uniform.
 typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
@@ -123,8 +104,6 @@ constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
 constexpr int kDppRowBcast15 = 0x142;
 constexpr int kDppRowBcast31 = 0x143;
-constexpr int kDppRowRor4 = 0x124;
-constexpr int kDppRowRor8 = 0x128;
 
 // Lanes of rows outside ROW_MASK read 0.  With a zero `old` and bound_ctrl
 // set, the compiler folds the move into the consuming add or max
@@ -179,43 +158,15 @@ __device__ inline float half_hi(uint32_t w) {
 
 __device__ inline float4 ldq4(const_f32_ptr p) { return make_float4(p[0], p[1], p[2], p[3]); }
 
-// Touch every 64-byte line of this group's query rows with scalar loads and
-// wait once (one round trip, overlapping the first tile's loads), so the
-// chunked scalar loads of the score phase hit the scalar cache.
-template <int N>
-__device__ inline void warm_query(const float* qg) {
-    constexpr int LINES = N / 16;
-    const_f32_ptr p = (const_f32_ptr)qg;
-    asm volatile("" : "+s"(p));
-    float t[LINES];
-#pragma unroll
-    for (int c = 0; c < LINES; ++c) t[c] = p[c * 16];
-#pragma unroll
-    for (int c = 0; c < LINES; ++c) asm volatile("" ::"s"(t[c]));
-}
-
 __device__ inline float sbyte(uint32_t w, int e) { return (float)(int8_t)(w >> (8 * e)); }
 
 template <int D>
 struct Geo {
-    static constexpr int NB = D / 32;                // q8_0 blocks per head
-    static constexpr int CB = 34 * NB;               // bytes of one head of one row
-    static constexpr int CW = CB / 4;                // ... in dwords
-    static constexpr int E = (CB % 8 == 0) ? 8 : 4;  // load unit
-    static constexpr int U = CB / E;                 // units per chunk (17)
-    static constexpr int LPR = D / 16;               // value-phase lanes per row
-    static constexpr int RPP = 64 / LPR;             // value-phase rows per pass
-    static_assert(U == 17, "chunk must be 17 load units");
-    static_assert(CB % 4 == 0, "chunk must be whole dwords");
+    static constexpr int NB = D / 32;   // q8_0 blocks per head
+    static constexpr int CB = 34 * NB;  // bytes of one head of one row
 };
 
-template <int D>
-struct TileRegs {
-    typedef typename std::conditional<Geo<D>::E == 8, u32x2, uint32_t>::type unit_t;
-    unit_t u[17];
-};
-
-// Buffer descriptor for head g of the 64-row sub-tile starting at row0 of one
+// Buffer descriptor for head g of the 64-row tile starting at row0 of one
 // tensor (K or V).  Its range ends with head g's chunk in the last readable
 // row, so loads past the segment return zeros instead of touching memory.
 template <int D>
@@ -227,357 +178,15 @@ __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, const Se
     return make_rsrc(base + head_off, lim);
 }
 
-// Load-unit layout of one 64-row sub-tile of one head (17 units per row):
-//   instruction i < 16: rows 4i .. 4i+3, lane -> (row 4i + lane/16, unit lane%16)
-//   instruction 16    : every row's last unit, lane -> (row lane, unit 16)
-// so per-lane offsets are affine in i (one VGPR each) and each of the first 16
-// instructions reads four contiguous 128-byte runs.
-struct TileOffsets {
-    int32_t g_main;   // global byte offset of (row lane/16, unit lane%16)
-    int32_t g_last;   // global byte offset of (row lane, unit 16)
-    int32_t l_main;   // LDS byte offset of the same units in [64][17] packed rows
-    int32_t l_last;
-};
-
-template <int D>
-__device__ inline TileOffsets tile_offsets(int lane, int32_t stride) {
-    constexpr int E = Geo<D>::E;
-    TileOffsets t;
-    t.g_main = (lane >> 4) * stride + (lane & 15) * E;
-    t.g_last = lane * stride + 16 * E;
-    t.l_main = (17 * (lane >> 4) + (lane & 15)) * E;
-    t.l_last = (17 * lane + 16) * E;
-    return t;
-}
-
-template <int D>
-__device__ inline void load_tile(TileRegs<D>& r, __amdgpu_buffer_rsrc_t rs, const TileOffsets& o, int32_t stride) {
-#pragma unroll
-    for (int i = 0; i < 17; ++i) {
-        const int32_t voff = (i < 16) ? o.g_main + 4 * i * stride : o.g_last;
-        if constexpr (Geo<D>::E == 8) r.u[i] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, 0, 0);
-        else r.u[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, 0, 0);
-    }
-}
-
-template <int D>
-__device__ inline void store_tile(const TileRegs<D>& r, uint8_t* t, const TileOffsets& o) {
-    using unit_t = typename TileRegs<D>::unit_t;
-    constexpr int E = Geo<D>::E;
-#pragma unroll
-    for (int i = 0; i < 17; ++i) {
-        const int32_t loff = (i < 16) ? o.l_main + 68 * i * E : o.l_last;
-        *(unit_t*)(t + loff) = r.u[i];
-    }
-}
-
-template <int D, int G, int NW>
-__global__ void __launch_bounds__(64 * NW) decode_kernel(const LaunchArgs A) {
-    constexpr int kThreads = 64 * NW;
-    using G_ = Geo<D>;
-    constexpr int NB = G_::NB, CB = G_::CB, CW = G_::CW, LPR = G_::LPR, RPP = G_::RPP;
-    static_assert(NB % 2 == 0, "head_dim must be a multiple of 64");
-    constexpr int GP = (G + 3) / 4 * 4;  // p row padded to float4
-
-    __shared__ __attribute__((aligned(16))) uint8_t s_tile[NW][2][kSubRows * CB];
-    __shared__ __attribute__((aligned(16))) float s_p[NW][kSubRows][GP];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // Workgroups go round-robin over the 8 XCDs; give each XCD a contiguous
-    // run of items so that the KV heads of one row range share an L2.
-    const int nblk = gridDim.x;
-    const int item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    if (item >= A.n_items) return;
-    const int lsplit = item / A.n_head_kv;
-    const int g = item - lsplit * A.n_head_kv;
-    int s = 0;
-    while (s + 1 < A.n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
-    const SeqDesc& SQ = A.seq[s];
-    int sp = lsplit - SQ.split_base;
-    int sgi = 0;
-    if (sp >= SQ.seg[0].n_split) {
-        sp -= SQ.seg[0].n_split;
-        sgi = 1;
-    }
-    const SegDesc& SG = SQ.seg[sgi];
-    const int r_begin = SG.row_lo + sp * A.split_rows;
-    const int r_end = min(r_begin + A.split_rows, SG.row_lo + SG.n_vis);
-    const int n_sub = (r_end - r_begin + kSubRows - 1) / kSubRows;
-    const int n_head_q = A.n_head_kv * G;
-    const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D;
-
-    const TileOffsets toff = tile_offsets<D>(lane, SG.stride);
-
-    uint8_t* tk = s_tile[wave][0];
-    uint8_t* tv = s_tile[wave][1];
-    float(*pw)[GP] = s_p[wave];
-
-    float m[G], l[G], o[G][16];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) o[h][k] = 0.f;
-    }
-
-    // value-phase lane roles
-    const int vpart = lane % LPR;            // which 16 dims
-    const int vrs = lane / LPR;              // row slot within a pass
-    const int vb = vpart >> 1;               // block
-    const int vsb = 34 * vb + 2 + 16 * (vpart & 1);  // first code byte within the chunk
-    const int vdw = vsb >> 2;                // first dword to read
-    const int vsh = vsb & 3;                 // 0 or 2
-    const int vdw4 = min(vdw + 4, CW - 1);   // 5th dword (only used when vsh == 2)
-
-    TileRegs<D> regs;
-    int t = wave;
-    if (t < n_sub) {
-        // first sub-tile: K and V in flight together
-        TileRegs<D> regs_v;
-        load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, r_begin + t * kSubRows), toff, SG.stride);
-        load_tile<D>(regs_v, tile_rsrc<D>(SG.v, SG, g, r_begin + t * kSubRows), toff, SG.stride);
-        warm_query<G * D>(qg);
-        store_tile<D>(regs, tk, toff);
-        store_tile<D>(regs_v, tv, toff);
-    }
-    for (; t < n_sub; t += NW) {
-        const int row0 = r_begin + t * kSubRows;
-        const int nv = min(kSubRows, r_end - row0);
-        const bool has_next = t + NW < n_sub;
-        // next K and V in flight during this sub-tile's scores and values
-        TileRegs<D> regs_v;
-        if (has_next) {
-            load_tile<D>(regs, tile_rsrc<D>(SG.k, SG, g, row0 + NW * kSubRows), toff, SG.stride);
-            load_tile<D>(regs_v, tile_rsrc<D>(SG.v, SG, g, row0 + NW * kSubRows), toff, SG.stride);
-        }
-        wave_lds_sync();
-
-        // ---- scores, one lane per row
-        // The query is read with scalar loads, 4 dims x G heads at a time,
-        // one chunk ahead of its use.  Empty asm statements pin the order:
-        // the accumulators of chunk c-1 pass through one before the address
-        // of chunk c+1 is formed, so the loads are neither hoisted nor
-        // widened and the query never occupies more than two chunks of SGPRs.
-        float sc[G];
-        {
-            const uint32_t* rp = (const uint32_t*)(tk + lane * CB);
-            constexpr int NCH = D / 4;
-            float4 qc[G];
-            {
-                const_f32_ptr qp = (const_f32_ptr)qg;
-                asm volatile("" : "+s"(qp));
-#pragma unroll
-                for (int h = 0; h < G; ++h) qc[h] = ldq4(qp + h * D);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) sc[h] = 0.f;
-            uint32_t wn[9];
-#pragma unroll
-            for (int j = 0; j < 9; ++j) wn[j] = rp[j];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                // block b: scale at byte 34b, codes at bytes 34b+2 .. 34b+33
-                uint32_t w[9];
-#pragma unroll
-                for (int j = 0; j < 9; ++j) w[j] = wn[j];
-                if (b + 1 < NB) {
-                    const int nb0 = ((b + 1) % 2 == 0) ? 17 * (b + 1) / 2 : (17 * (b + 1) - 1) / 2;
-#pragma unroll
-                    for (int j = 0; j < 9; ++j) wn[j] = rp[nb0 + j];
-                }
-                float dot[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) dot[h] = 0.f;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int c = 8 * b + kk;
-                    // chunk order: every head's accumulator passes through an
-                    // empty asm before the next chunk's address is formed
-#pragma unroll
-                    for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
-                    float4 qn[G];
-                    if (c + 1 < NCH) {
-                        const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
-                        asm volatile("" : "+s"(qp));
-#pragma unroll
-                        for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
-                    }
-                    const uint32_t x = (b % 2 == 0) ? __builtin_amdgcn_alignbyte(w[kk + 1], w[kk], 2) : w[kk + 1];
-                    const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        dot[h] = fmaf(qc[h].x, k0, dot[h]);
-                        dot[h] = fmaf(qc[h].y, k1, dot[h]);
-                        dot[h] = fmaf(qc[h].z, k2, dot[h]);
-                        dot[h] = fmaf(qc[h].w, k3, dot[h]);
-                    }
-                    if (c + 1 < NCH) {
-#pragma unroll
-                        for (int h = 0; h < G; ++h) qc[h] = qn[h];
-                    }
-                }
-                const float d = (b % 2 == 0) ? half_lo(w[0]) : half_hi(w[0]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) sc[h] = fmaf(d, dot[h], sc[h]);
-            }
-#pragma unroll
-            for (int h = 0; h < G; ++h) sc[h] = (lane < nv) ? sc[h] * A.scale_log2e : -INFINITY;
-        }
-
-        // ---- online softmax (exp2 domain)
-        {
-            float mt[G];
-            bool grow = false;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                mt[h] = wave_max(sc[h]);
-                grow |= mt[h] > m[h];
-            }
-            if (grow) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float mn = fmaxf(m[h], mt[h]);
-                    const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-                    l[h] *= alpha;
-#pragma unroll
-                    for (int k = 0; k < 16; ++k) o[h][k] *= alpha;
-                    m[h] = mn;
-                }
-            }
-            float pr[GP];
-#pragma unroll
-            for (int h = 0; h < GP; ++h) pr[h] = 0.f;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                pr[h] = __builtin_amdgcn_exp2f(sc[h] - m[h]);
-                l[h] += pr[h];
-            }
-#pragma unroll
-            for (int h = 0; h < GP; h += 4) *(float4*)&pw[lane][h] = make_float4(pr[h], pr[h + 1], pr[h + 2], pr[h + 3]);
-        }
-        wave_lds_sync();
-        if (has_next) store_tile<D>(regs, tk, toff);
-
-        // ---- values, 16 dims per lane, RPP rows per pass
-#pragma unroll 2
-        for (int pass = 0; pass < LPR; ++pass) {
-            const int r = pass * RPP + vrs;
-            const uint32_t* rowp = (const uint32_t*)(tv + r * CB);
-            uint32_t w0 = rowp[vdw], w1 = rowp[vdw + 1], w2 = rowp[vdw + 2], w3 = rowp[vdw + 3], w4 = rowp[vdw4];
-            uint32_t a0 = __builtin_amdgcn_alignbyte(w1, w0, vsh);
-            uint32_t a1 = __builtin_amdgcn_alignbyte(w2, w1, vsh);
-            uint32_t a2 = __builtin_amdgcn_alignbyte(w3, w2, vsh);
-            uint32_t a3 = __builtin_amdgcn_alignbyte(w4, w3, vsh);
-            const uint16_t dbits = *(const uint16_t*)(tv + r * CB + 34 * vb);
-            float d = (float)__builtin_bit_cast(_Float16, dbits);
-            d = (r < nv) ? d : 0.f;
-            float c[G];
-#pragma unroll
-            for (int h = 0; h < G; h += 4) {
-                const float4 pv = *(const float4*)&pw[r][h];
-                c[h] = pv.x * d;
-                if (h + 1 < G) c[h + 1] = pv.y * d;
-                if (h + 2 < G) c[h + 2] = pv.z * d;
-                if (h + 3 < G) c[h + 3] = pv.w * d;
-            }
-            const uint32_t aw[4] = {a0, a1, a2, a3};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float vv = sbyte(aw[kk], e);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) o[h][4 * kk + e] = fmaf(c[h], vv, o[h][4 * kk + e]);
-                }
-            }
-        }
-        wave_lds_sync();
-        if (has_next) store_tile<D>(regs_v, tv, toff);
-    }
-
-    // ---- wave state: total l; o summed over the row slots of each 16-lane
-    // row by DPP rotations, the four rows then go through LDS.
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        l[h] = wave_sum(l[h]);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            float x = o[h][k];
-            if constexpr (LPR == 4) x += dpp<kDppRowRor4>(x);
-            x += dpp<kDppRowRor8>(x);
-            o[h][k] = x;
-        }
-    }
-
-    // ---- merge the waves in LDS (reuses the tile memory)
-    __syncthreads();
-    float* mw = (float*)&s_tile[0][0][0];   // [NW][G]
-    float* lw = mw + NW * G;            // [NW][G]
-    float* ow = lw + NW * G;            // [NW][4 rows][G][D]
-    static_assert((2 * NW * G + NW * 4 * G * D) * 4 <= (int)sizeof(s_tile), "merge area");
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mw[wave * G + h] = m[h];
-            lw[wave * G + h] = l[h];
-        }
-    }
-    if ((lane & 15) < LPR) {
-        const int row16 = lane >> 4;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float* dst = ow + (((size_t)wave * 4 + row16) * G + h) * D + vpart * 16;
-#pragma unroll
-            for (int k = 0; k < 16; k += 4) *(float4*)(dst + k) = make_float4(o[h][k], o[h][k + 1], o[h][k + 2], o[h][k + 3]);
-        }
-    }
-    __syncthreads();
-
-    const int hq0 = g * G;  // first query head of this group
-    const bool single = SQ.n_split == 1;
-    const int abs_split = A.split_off + lsplit;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int h = idx / D, i = idx - (idx / D) * D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) M = fmaxf(M, mw[w2 * G + h]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const float mv = mw[w2 * G + h];
-            const float a = (mv == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mv - M);
-            L = fmaf(a, lw[w2 * G + h], L);
-            float ov = 0.f;
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) ov += ow[(((size_t)w2 * 4 + r4) * G + h) * D + i];
-            O = fmaf(a, ov, O);
-        }
-        if (single) {
-            write_final(A, D, (size_t)s * n_head_q + hq0 + h, i, O, M, L, i == 0);
-        } else {
-            const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-            A.po[pi * D + i] = O;
-            if (i == 0) {
-                A.pm[pi] = M;
-                A.pl[pi] = L;
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Block-sliced form of the decode kernel (the default).  A workgroup has one
-// wave per q8_0 block of the head (D / 32 waves) and walks the split's rows
-// in 64-row tiles, all waves on the same tile:
+// The decode kernel.  A workgroup has one wave per q8_0 block of the head
+// (D / 32 waves) and walks the split's rows in 64-row tiles, all waves on the
+// same tile:
 //   * wave w loads only block w of each row (a 9-dword window around its 34
 //     bytes) for K and V, one tile ahead in registers, staged through a
 //     wave-private LDS tile;
 //   * scores: one lane per row, the block's 32 codes against the query slice
-//     (staged in LDS, read back 4 dims x G heads at a time), times the block
+//     (read 4 dims x G heads at a time, from LDS or SGPRs), times the block
 //     scale; the D / 32 block partials meet in LDS at one workgroup barrier
 //     per tile (LDS-only fences, so the prefetch stays in flight), and every
 //     wave sums them in the same order, so all waves hold identical scores;
@@ -654,7 +263,7 @@ __device__ inline __amdgpu_buffer_rsrc_t vtile_rsrc(const SegDesc& sg, int g, in
     return make_rsrc(sg.v + head_off, lim);
 }
 
-template <int D, int G, int VT, int ODD>
+template <int D, int G, int VT, int QS, int ODD>
 __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int g,
                                            const int r_begin, const int r_end, const bool single,
                                            const int abs_split, const int wave, const int lane, uint32_t* tk,
@@ -711,16 +320,21 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     // K of a tile is staged before its scores, V only after them, so the
     // scores of the first tile start as soon as its K has arrived; the next
     // tile's K and V are in flight in registers meanwhile.
-    // The wave's query slice (G heads x 32 dims) goes to LDS with one vector
-    // load per lane, issued first; the scores read it back as wave-uniform
-    // float4s.  (Scalar loads of a query that is cold in the scalar cache
-    // serialise on its misses: several microseconds per call.)
+    // The wave's query slice (G heads x 32 dims) is read by the scores as
+    // wave-uniform chunks of 4 dims x G heads, from one of two places:
+    //  QS = 0: LDS, filled with one vector load per lane issued first, and
+    //          read back as broadcast float4s (for workgroups alone on their
+    //          CU: the scalar loads below would miss a cold scalar cache
+    //          there, several microseconds per call);
+    //  QS = 1: SGPRs, by scalar loads one chunk ahead (once several
+    //          workgroups share a CU: no LDS traffic for the query, which
+    //          would otherwise be about half of the kernel's LDS reads).
     float4 qv4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (lane < G * 8) qv4 = *(const float4*)(qg + (lane >> 3) * D + 4 * (lane & 7));
+    if (!QS && lane < G * 8) qv4 = *(const float4*)(qg + (lane >> 3) * D + 4 * (lane & 7));
     uint32_t rk[9], rv[VW];
     load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
     load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, r_begin), voffv);
-    if (lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
+    if (!QS && lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
     store_win(rk, tk, lane);
 
     for (int t = 0; t < n_tiles; ++t) {
@@ -737,21 +351,37 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             uint32_t w[9];
 #pragma unroll
             for (int j = 0; j < 9; ++j) w[j] = rp[j];
-            // query chunks of 4 dims x G heads from LDS, each read just before
-            // its FMAs; the empty asm statements keep the reads from being
-            // hoisted, so the query holds one chunk of registers.  (G = 5: 125
-            // VGPRs instead of 140 when reading one chunk ahead, so four
-            // workgroups fit a CU instead of three, and their waves hide the
-            // LDS latency that the read-ahead used to.)
+            // Query chunks of 4 dims x G heads.  From LDS (QS = 0) each is read
+            // just before its FMAs: the empty asm statements keep the reads
+            // from being hoisted, so the query holds one chunk of VGPRs (G = 5:
+            // 125 VGPRs instead of 140 when reading one chunk ahead, so four
+            // workgroups fit a CU instead of three).  From SGPRs (QS = 1) the
+            // scalar loads run one chunk ahead, their order pinned the same way.
             float dot[G];
 #pragma unroll
             for (int h = 0; h < G; ++h) dot[h] = 0.f;
+            float4 qn[G];
+            if constexpr (QS) {
+                const_f32_ptr qp = (const_f32_ptr)qg;
+                asm volatile("" : "+s"(qp));
+#pragma unroll
+                for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
+            }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
                 float4 qc[G];
-                {
+                if constexpr (QS) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) qc[h] = qn[h];
+                    if (c + 1 < 8) {
+                        const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
+                        asm volatile("" : "+s"(qp));
+#pragma unroll
+                        for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
+                    }
+                } else {
                     int off = 4 * c;
                     asm volatile("" : "+v"(off));
 #pragma unroll
@@ -918,14 +548,14 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     }
 }
 
-template <int D, int G, int VT>
+template <int D, int G, int VT, int QS>
 __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A) {
     using S_ = Slice<D, G>;
     constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
     __shared__ __attribute__((aligned(16))) uint32_t s_kv[NB][2][T * 9];
     __shared__ __attribute__((aligned(16))) float s_x[2 * NB * G * 64];
     __shared__ __attribute__((aligned(16))) float s_c[NB][T * GP];
-    __shared__ __attribute__((aligned(16))) float s_q[NB][G * 32];
+    __shared__ __attribute__((aligned(16))) float s_q[NB][QS ? 4 : G * 32];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -949,10 +579,10 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
     const bool single = SQ.n_split == 1;
     const int abs_split = A.split_off + lsplit;
     if (wave & 1)
-        slice_body<D, G, VT, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+        slice_body<D, G, VT, QS, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
                                 s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
     else
-        slice_body<D, G, VT, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
+        slice_body<D, G, VT, QS, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
                                 s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
 }
 
@@ -1062,46 +692,31 @@ __global__ void __launch_bounds__(64 * (D / 32)) merge_kernel(const float* parts
 typedef void (*decode_fn)(const LaunchArgs);
 typedef void (*combine_fn)(const LaunchArgs, int32_t);
 
-template <int D, int NW>
-decode_fn pick_g(int G) {
-    switch (G) {
-        case 1: return decode_kernel<D, 1, NW>;
-        case 2: return decode_kernel<D, 2, NW>;
-        case 3: return decode_kernel<D, 3, NW>;
-        case 4: return decode_kernel<D, 4, NW>;
-        case 5: return decode_kernel<D, 5, NW>;
-        case 6: return decode_kernel<D, 6, NW>;
-        case 7: return decode_kernel<D, 7, NW>;
-        case 8: return decode_kernel<D, 8, NW>;
-    }
-    return nullptr;
-}
-
-decode_fn pick_decode(int D, int G, int NW) {
-    if (D == 128) return NW == 8 ? pick_g<128, 8>(G) : pick_g<128, 2>(G);
-    return NW == 8 ? pick_g<64, 8>(G) : pick_g<64, 2>(G);
-}
-
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
-template <int D, int VT>
+template <int D, int VT, int QS>
 decode_fn pick_slice_g(int G) {
     switch (G) {
-        case 1: return slice_kernel<D, 1, VT>;
-        case 2: return slice_kernel<D, 2, VT>;
-        case 3: return slice_kernel<D, 3, VT>;
-        case 4: return slice_kernel<D, 4, VT>;
-        case 5: return slice_kernel<D, 5, VT>;
-        case 6: return slice_kernel<D, 6, VT>;
-        case 7: return slice_kernel<D, 7, VT>;
-        case 8: return slice_kernel<D, 8, VT>;
+        case 1: return slice_kernel<D, 1, VT, QS>;
+        case 2: return slice_kernel<D, 2, VT, QS>;
+        case 3: return slice_kernel<D, 3, VT, QS>;
+        case 4: return slice_kernel<D, 4, VT, QS>;
+        case 5: return slice_kernel<D, 5, VT, QS>;
+        case 6: return slice_kernel<D, 6, VT, QS>;
+        case 7: return slice_kernel<D, 7, VT, QS>;
+        case 8: return slice_kernel<D, 8, VT, QS>;
     }
     return nullptr;
 }
 
-decode_fn pick_slice(int D, int G, int VT) {
-    if (VT) return D == 128 ? pick_slice_g<128, 1>(G) : pick_slice_g<64, 1>(G);
-    return D == 128 ? pick_slice_g<128, 0>(G) : pick_slice_g<64, 0>(G);
+template <int QS>
+decode_fn pick_slice_qs(int D, int G, int VT) {
+    if (VT) return D == 128 ? pick_slice_g<128, 1, QS>(G) : pick_slice_g<64, 1, QS>(G);
+    return D == 128 ? pick_slice_g<128, 0, QS>(G) : pick_slice_g<64, 0, QS>(G);
+}
+
+decode_fn pick_slice(int D, int G, int VT, bool scalar_query) {
+    return scalar_query ? pick_slice_qs<1>(D, G, VT) : pick_slice_qs<0>(D, G, VT);
 }
 
 }  // namespace
@@ -1137,7 +752,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    const decode_fn dk = p.kernel == 3 ? pick_slice(a->head_dim, p.group, a->v_type) : pick_decode(a->head_dim, p.group, p.waves);
+    const decode_fn dk = pick_slice(a->head_dim, p.group, a->v_type, p.scalar_query);
     const combine_fn ck = pick_combine(a->head_dim);
     if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 

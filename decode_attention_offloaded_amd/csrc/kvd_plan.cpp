@@ -12,25 +12,34 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Workgroups of the block-sliced kernel for splits of `rows` rows: every
+// visible range cut into splits, times the KV heads.
+int64_t slice_workgroups(const AttendPlan& p, int n_head_kv, int64_t rows) {
+    int64_t wgs = 0;
+    for (const SeqPlan& sp : p.seq) wgs += ceil_div(sp.seg[0].n_vis, rows) + ceil_div(sp.seg[1].n_vis, rows);
+    return wgs * n_head_kv;
+}
+
+// Relative time per unit of work when the busiest CU runs `per_cu` workgroups:
+// one workgroup per CU (one wave per SIMD) hides little latency; up to four
+// are resident at once (registers and LDS allow four), beyond that they queue.
+int64_t slice_occupancy_cost(int64_t per_cu) {
+    return per_cu == 1 ? 160 : per_cu == 2 ? 100 : per_cu == 3 ? 93 : 87;
+}
+
 // Tiles (64 rows) per split for the block-sliced kernel, all waves of a
-// workgroup sharing each tile.  A candidate of k tiles gives W workgroups
-// (every visible range cut into splits of k tiles, times the KV heads); the
+// workgroup sharing each tile.  A candidate of k tiles gives W workgroups; the
 // busiest CU then runs ceil(W / CUs) of them, each costing k tiles plus
-// kSliceOverheadTiles of fixed work (start-up, fold, partial write), and 1.6
-// times that when each CU holds a single workgroup (one wave per SIMD hides
-// little latency).  The cheapest candidate wins, the larger on a tie.  On one
-// sequence of 1024 ... 65536 rows x 8 KV heads this picks the measured
-// fastest split or one within 2%.
+// kSliceOverheadTiles of fixed work (start-up, fold, partial write), weighted
+// by slice_occupancy_cost.  The cheapest candidate wins, the larger on a tie.
+// On one sequence of 1024 ... 131072 rows x 8 KV heads this picks the
+// measured fastest split or one within 1%.
 int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis) {
-    const int64_t max_k = std::max<int64_t>(1, ceil_div(max_vis, kSubRows));
+    const int64_t max_k = std::max<int64_t>(1, ceil_div(max_vis, kTileRows));
     int64_t best_k = 1, best_cost = INT64_MAX;
     for (int64_t k = 1; k <= max_k;) {
-        const int64_t rows = k * kSubRows;
-        int64_t wgs = 0;
-        for (const SeqPlan& sp : p.seq) wgs += ceil_div(sp.seg[0].n_vis, rows) + ceil_div(sp.seg[1].n_vis, rows);
-        wgs *= n_head_kv;
-        const int64_t per_cu = ceil_div(wgs, kCUs);
-        const int64_t cost = (per_cu == 1 ? 16 : 10) * per_cu * (k + kSliceOverheadTiles);
+        const int64_t per_cu = ceil_div(slice_workgroups(p, n_head_kv, k * kTileRows), kCUs);
+        const int64_t cost = slice_occupancy_cost(per_cu) * per_cu * (k + kSliceOverheadTiles);
         if (cost <= best_cost) {
             best_cost = cost;
             best_k = k;
@@ -59,7 +68,7 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
         return fail(KVD_EINVAL, "head_dim %d not supported (64 or 128)", a->head_dim);
     if (a->n_seg != 1 && a->n_seg != 2) return fail(KVD_EINVAL, "n_seg %d must be 1 or 2", a->n_seg);
     if (a->window < 0) return fail(KVD_EINVAL, "window %d < 0", a->window);
-    if (a->split_rows < 0 || a->split_rows % kSubRows != 0 || a->split_rows > (1 << 24))
+    if (a->split_rows < 0 || a->split_rows % kTileRows != 0 || a->split_rows > (1 << 24))
         return fail(KVD_EINVAL, "split_rows %d must be 0 or a positive multiple of 64", a->split_rows);
     if (!isfinite(a->scale)) return fail(KVD_EINVAL, "scale is not finite");
     if (!a->q || !a->segs) return fail(KVD_EINVAL, "q and segs must not be NULL");
@@ -74,13 +83,11 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     const int64_t v_row_bytes = (int64_t)a->n_head_kv * (D / 32) * (a->v_type == KVD_TYPE_Q4_0 ? 18 : 34);
     const int64_t align = (D == 128) ? 8 : 4;
     const int64_t v_align = a->v_type == KVD_TYPE_Q4_0 ? 4 : align;
-    bool strides_differ = false;
 
     p->group = G;
     p->chunk_bytes = chunk;
     p->seq.assign(a->n_seq, SeqPlan{});
 
-    int64_t total_sub = 0;
     for (int s = 0; s < a->n_seq; ++s) {
         const kvd_kv_seg* segs = a->segs + (size_t)s * a->n_seg;
         for (int j = 0; j < a->n_seg; ++j) {
@@ -104,7 +111,6 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
             if ((uintptr_t)g.v % v_align || vs % v_align)
                 return fail(KVD_EINVAL, "seq %d seg %d: v and its row stride must be %lld-byte aligned", s, j,
                             (long long)v_align);
-            strides_differ |= vs != g.row_stride;
         }
         const kvd_kv_seg& last = segs[a->n_seg - 1];
         int64_t qp;
@@ -135,7 +141,6 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
                 pl.n_vis = (int32_t)(hi - lo);
             }
             vis += pl.n_vis;
-            total_sub += ceil_div(pl.n_vis, kSubRows);
         }
         if (vis < 1) return fail(KVD_EINVAL, "seq %d: no row is visible to the query at position %lld", s,
                                  (long long)qp);
@@ -144,36 +149,23 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
-    // Kernel and waves per workgroup.  The block-sliced kernel (one wave per
-    // q8_0 block, D / 32 waves sharing each tile) by default; the lane-per-row
-    // kernel (8 waves, one workgroup per CU, waves merged in LDS) for a single
-    // contiguous range of more than kSliceMaxWork tile-heads, where its longer
-    // splits are slightly faster.  Batches of segments balance better over the
-    // block-sliced kernel's smaller workgroups (measured: 73 us against 113 us
-    // for 16 sequences of 1024 ... 20082 rows in two segments each).
-    const int64_t work = total_sub * a->n_head_kv;
-    int ranges = 0;
-    for (const SeqPlan& sp : p->seq) ranges += (sp.seg[0].n_vis > 0) + (sp.seg[1].n_vis > 0);
-    p->kernel = kKernelChoice != 0 ? kKernelChoice : (work > kSliceMaxWork && ranges == 1 ? 1 : 3);
-    // only the block-sliced kernel reads q4_0 V or V rows of their own stride
-    if (a->v_type != KVD_TYPE_Q8_0 || strides_differ) p->kernel = 3;
-    p->waves = p->kernel == 3 ? a->head_dim / 32 : (work >= kTargetWaves) ? 8 : 2;
+    // one wave per q8_0 block of the head
+    p->waves = a->head_dim / 32;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
-        if (p->kernel == 3) {
-            split_rows = (int64_t)kSubRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis);
-        } else {
-            const int64_t per_wave = std::max<int64_t>(1, ceil_div(work, kTargetWaves));
-            split_rows = (int64_t)kSubRows * p->waves * per_wave;
-        }
+        split_rows = (int64_t)kTileRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis);
         // segments split separately: allow one extra split per segment
-        const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kSubRows) * kSubRows;
+        const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kTileRows) * kTileRows;
         split_rows = std::max(split_rows, floor_rows);
         // up to kOneSplitRows visible rows per sequence: one split, no combine launch
-        if (max_vis <= kOneSplitRows) split_rows = std::max<int64_t>(split_rows, ceil_div(max_vis, kSubRows) * kSubRows);
+        if (max_vis <= kOneSplitRows) split_rows = std::max<int64_t>(split_rows, ceil_div(max_vis, kTileRows) * kTileRows);
         if (split_rows > (1 << 24)) split_rows = 1 << 24;
     }
     p->split_rows = (int32_t)split_rows;
+    // Query by scalar loads once several workgroups share a CU (no LDS traffic
+    // for it); from LDS when each CU holds one workgroup, whose scalar loads
+    // would find a cold scalar cache.
+    p->scalar_query = ceil_div(slice_workgroups(*p, a->n_head_kv, split_rows), kCUs) >= 2;
 
     int64_t base = 0;
     int32_t max_splits = 0;

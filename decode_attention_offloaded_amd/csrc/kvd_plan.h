@@ -10,18 +10,9 @@
 
 namespace kvd {
 
-constexpr int kSubRows = 64;            // rows per wave sub-tile of the lane-per-row kernel
-// Decode kernel choice: 0 = by problem shape (lane-per-row for one visible
-// range of more than kSliceMaxWork tile-heads, block-sliced otherwise); 1 or
-// 3 forces one.
-#ifndef KVD_DECODE_KERNEL
-#define KVD_DECODE_KERNEL 0
-#endif
-constexpr int kKernelChoice = KVD_DECODE_KERNEL;
-constexpr int64_t kSliceMaxWork = 8192;  // 64-row tiles x KV heads
+constexpr int kTileRows = 64;           // rows per tile of the decode kernel (split sizes are multiples)
 constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
-constexpr int64_t kTargetWaves = 2048;  // 256 CUs x 8 waves: enough sub-tiles to fill the chip
 constexpr int64_t kCUs = 256;              // compute units of the device
 constexpr int64_t kSliceOverheadTiles = 3;  // block-sliced fixed work per workgroup, in tiles
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
@@ -44,8 +35,8 @@ struct AttendPlan {
     int32_t group;        // G = n_head_q / n_head_kv
     int32_t chunk_bytes;  // bytes of one head of one row: head_dim / 32 * 34
     int32_t split_rows;
-    int32_t waves;        // waves per decode workgroup
-    int32_t kernel;       // 3: block-sliced kernel (one wave per q8_0 block); 1: lane-per-row scores
+    int32_t waves;        // waves per decode workgroup (one per q8_0 block of a head)
+    bool scalar_query;    // query chunks by scalar loads (else from LDS)
     int32_t max_splits;   // largest per-sequence split count
     int64_t total_splits;
     std::vector<SeqPlan> seq;

@@ -119,7 +119,7 @@ static void fuzz_plan(Rng& r) {
     CHECK(rc == KVD_OK || rc == KVD_EINVAL, "plan rc %d", rc);
     if (rc != KVD_OK) return;
     ++g_plan_ok;
-    CHECK(p.kernel == 1 || p.kernel == 3, "kernel %d", p.kernel);
+    CHECK(p.waves == a.head_dim / 32, "waves %d", p.waves);
     CHECK(p.split_rows >= 64 && p.split_rows % 64 == 0, "split_rows %d", p.split_rows);
     if (a.split_rows > 0) CHECK(p.split_rows == a.split_rows, "split_rows %d != asked %d", p.split_rows, a.split_rows);
     int64_t base = 0, max_split = 0;
@@ -161,6 +161,8 @@ static void fuzz_plan(Rng& r) {
         if (n > max_split) max_split = n;
     }
     CHECK(base == p.total_splits && max_split == p.max_splits, "totals");
+    // query by scalar loads exactly when some CU runs two or more workgroups
+    CHECK(p.scalar_query == ((p.total_splits * a.n_head_kv + 255) / 256 >= 2), "query source");
     if (p.max_splits <= 1) {
         CHECK(p.ws_bytes == 0, "single splits need no workspace");
     } else {

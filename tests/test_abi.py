@@ -116,18 +116,18 @@ def _splits(n_rows_list, seg_rows=None):
 
 
 @pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (16384, 64), (32768, 64),
-                                      (65536, 64), (131072, 32)])
+                                      (65536, 64), (131072, 128)])
 def test_split_plan_single_sequence(n, splits):
     """Splits per KV head on one sequence of n rows x 8 KV heads (the measured
-    fastest: 64-row splits up to 2048 rows, then about two workgroups per CU;
-    131072 rows go to the lane-per-row kernel, 4096 rows per workgroup)."""
+    fastest or within 2% of it: 64-row splits up to 2048 rows, then two
+    workgroups per CU up to 65536 rows, four at 131072 rows)."""
     assert _splits([n]) == splits
 
 
 def test_split_plan_batch():
-    """16 sequences in two segments each: 1024-row splits, so 92 in all."""
+    """16 sequences in two segments each: 768-row splits, so 120 in all."""
     lens = [1024, 1024, 1862, 1990, 2813, 3712, 3769, 4264, 5376, 5801, 6363, 6588, 7292, 8678, 9634, 10041]
-    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 1024) + -(-(n - n // 2) // 1024) for n in lens) == 92
+    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 768) + -(-(n - n // 2) // 768) for n in lens) == 120
 
 
 def test_workspace_too_small_is_rejected():

@@ -166,23 +166,24 @@ def test_long_context_sampled_heads(oracle):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("g_size", [1, 2, 4, 8])
 def test_long_range_every_group_size(oracle, d, g_size):
-    """One range of 65600 rows x 8 KV heads (8200 tile-heads, just past the
-    block-sliced kernel's limit for a single range, ragged last tile) runs on
-    the lane-per-row kernel; the same rows in two segments run on the
-    block-sliced kernel.  Sampled KV heads of both against the oracle, for
-    every GQA group size the kernels are built for."""
+    """One range of 65600 rows x 8 KV heads (ragged last tile), three ways:
+    as planned (several workgroups per CU, so the query comes by scalar
+    loads), in 2112-row splits (32 per KV head: one workgroup per CU, the
+    query from LDS), and in two segments.  Sampled KV heads of each against
+    the oracle, for every GQA group size the kernel is built for."""
     n, hkv = 65600, 8
     hq = hkv * g_size
     rng, k, v = make_cache(7000 + d + g_size, n, hkv, d)
     q = inputs.random_q(rng, 1, hq, d)
     one = gpu_attend(q, [[(k, v, 0)]], hkv)
+    wide = gpu_attend(q, [[(k, v, 0)]], hkv, split_rows=2112)
     h = n // 3
     two = gpu_attend(q, [[(k[:h], v[:h], 0), (k[h:], v[h:], h)]], hkv)
     for g in (1, hkv - 2):
         ks, vs = head_slice(k, g, hkv, d), head_slice(v, g, hkv, d)
         ref = oracle.attend(q[:, g * g_size:(g + 1) * g_size], [[(ks, vs, 0)]], 1, d, threads=8)
-        check(one[:, g * g_size:(g + 1) * g_size], ref)
-        check(two[:, g * g_size:(g + 1) * g_size], ref)
+        for out in (one, wide, two):
+            check(out[:, g * g_size:(g + 1) * g_size], ref)
 
 
 @pytest.mark.parametrize("n,v_type", [(4096, 0), (300, 0), (200000 // 64 * 64, 0), (4096, 1)])
