@@ -694,17 +694,25 @@ typedef void (*combine_fn)(const LaunchArgs, int32_t);
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
+// The kernel for group G, or null for a scalar query beyond
+// kScalarQueryMaxGroup (the plan never asks for one).
+template <int D, int G, int VT, int QS>
+decode_fn slice_ptr() {
+    if constexpr (QS && G > kScalarQueryMaxGroup) return nullptr;
+    else return slice_kernel<D, G, VT, QS>;
+}
+
 template <int D, int VT, int QS>
 decode_fn pick_slice_g(int G) {
     switch (G) {
-        case 1: return slice_kernel<D, 1, VT, QS>;
-        case 2: return slice_kernel<D, 2, VT, QS>;
-        case 3: return slice_kernel<D, 3, VT, QS>;
-        case 4: return slice_kernel<D, 4, VT, QS>;
-        case 5: return slice_kernel<D, 5, VT, QS>;
-        case 6: return slice_kernel<D, 6, VT, QS>;
-        case 7: return slice_kernel<D, 7, VT, QS>;
-        case 8: return slice_kernel<D, 8, VT, QS>;
+        case 1: return slice_ptr<D, 1, VT, QS>();
+        case 2: return slice_ptr<D, 2, VT, QS>();
+        case 3: return slice_ptr<D, 3, VT, QS>();
+        case 4: return slice_ptr<D, 4, VT, QS>();
+        case 5: return slice_ptr<D, 5, VT, QS>();
+        case 6: return slice_ptr<D, 6, VT, QS>();
+        case 7: return slice_ptr<D, 7, VT, QS>();
+        case 8: return slice_ptr<D, 8, VT, QS>();
     }
     return nullptr;
 }

@@ -164,8 +164,8 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     p->split_rows = (int32_t)split_rows;
     // Query by scalar loads once several workgroups share a CU (no LDS traffic
     // for it); from LDS when each CU holds one workgroup, whose scalar loads
-    // would find a cold scalar cache.
-    p->scalar_query = ceil_div(slice_workgroups(*p, a->n_head_kv, split_rows), kCUs) >= 2;
+    // would find a cold scalar cache, and for groups too large for the SGPRs.
+    p->scalar_query = G <= kScalarQueryMaxGroup && ceil_div(slice_workgroups(*p, a->n_head_kv, split_rows), kCUs) >= 2;
 
     int64_t base = 0;
     int32_t max_splits = 0;

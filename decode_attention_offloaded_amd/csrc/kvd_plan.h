@@ -16,6 +16,9 @@ constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's a
 constexpr int64_t kCUs = 256;              // compute units of the device
 constexpr int64_t kSliceOverheadTiles = 3;  // block-sliced fixed work per workgroup, in tiles
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
+// Largest GQA group whose query chunks (this one and the next: 8 G floats)
+// stay in SGPRs without spilling; larger groups read the query from LDS.
+constexpr int kScalarQueryMaxGroup = 5;
 
 struct SegPlan {
     int32_t row_lo;   // first visible row (segment row index)

@@ -162,7 +162,9 @@ static void fuzz_plan(Rng& r) {
     }
     CHECK(base == p.total_splits && max_split == p.max_splits, "totals");
     // query by scalar loads exactly when some CU runs two or more workgroups
-    CHECK(p.scalar_query == ((p.total_splits * a.n_head_kv + 255) / 256 >= 2), "query source");
+    // and the group fits the SGPRs (at most 5 query heads per KV head)
+    CHECK(p.scalar_query == (a.n_head_q / a.n_head_kv <= 5 && (p.total_splits * a.n_head_kv + 255) / 256 >= 2),
+          "query source");
     if (p.max_splits <= 1) {
         CHECK(p.ws_bytes == 0, "single splits need no workspace");
     } else {

@@ -167,9 +167,9 @@ def test_long_context_sampled_heads(oracle):
 @pytest.mark.parametrize("g_size", [1, 2, 4, 8])
 def test_long_range_every_group_size(oracle, d, g_size):
     """One range of 65600 rows x 8 KV heads (ragged last tile), three ways:
-    as planned (several workgroups per CU, so the query comes by scalar
-    loads), in 2112-row splits (32 per KV head: one workgroup per CU, the
-    query from LDS), and in two segments.  Sampled KV heads of each against
+    as planned (several workgroups per CU, so groups of up to 5 take the
+    query by scalar loads), in 2112-row splits (32 per KV head: one workgroup
+    per CU, the query from LDS), and in two segments.  Sampled KV heads of each against
     the oracle, for every GQA group size the kernel is built for."""
     n, hkv = 65600, 8
     hq = hkv * g_size
