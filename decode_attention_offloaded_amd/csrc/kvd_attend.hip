@@ -559,25 +559,56 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Every argument at a fixed offset -- the counts, the output pointers and
+    // the first sequence's descriptors -- is read first and waited for once.
+    // The empty asm statements (after all the reads) keep the compiler from
+    // sinking these loads below the branches that use them, which costs a
+    // round trip to the arguments per branch level; a launch of one sequence
+    // then issues its first K/V loads after a single round trip (4096 rows:
+    // 11.9 us per call instead of 12.5).
+    SegDesc d0 = A.seq[0].seg[0], d1 = A.seq[0].seg[1];
+    int32_t seq_base = 0, seq_splits = A.seq[0].n_split;
+    const int32_t n_items = A.n_items, n_head_kv = A.n_head_kv, n_seq = A.n_seq;
+    const int32_t split_rows = A.split_rows, split_off = A.split_off;
+    const float scale = A.scale_log2e;
+    const float* const q = A.q;
+    float* const ptr[8] = {A.out, A.po, A.pm, A.pl, A.part_o, A.part_m, A.part_l, nullptr};
     const int nblk = gridDim.x;
+    asm volatile("" ::"s"(d0.k), "s"(d0.v), "s"(d0.stride), "s"(d0.row_lo), "s"(d0.n_vis), "s"(d0.n_split),
+                 "s"(d0.n_rows), "s"(d0.vstride));
+    asm volatile("" ::"s"(d1.k), "s"(d1.v), "s"(d1.stride), "s"(d1.row_lo), "s"(d1.n_vis), "s"(d1.n_rows),
+                 "s"(d1.vstride), "s"(seq_splits));
+    asm volatile("" ::"s"(n_items), "s"(n_head_kv), "s"(n_seq), "s"(split_rows), "s"(split_off), "s"(scale),
+                 "s"(q), "s"(nblk));
+    asm volatile("" ::"s"(ptr[0]), "s"(ptr[1]), "s"(ptr[2]), "s"(ptr[3]), "s"(ptr[4]), "s"(ptr[5]), "s"(ptr[6]));
     const int item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    if (item >= A.n_items) return;
-    const int lsplit = item / A.n_head_kv;
-    const int g = item - lsplit * A.n_head_kv;
+    if (item >= n_items) return;
+    const int lsplit = item / n_head_kv;
+    const int g = item - lsplit * n_head_kv;
     int s = 0;
-    while (s + 1 < A.n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
-    const SeqDesc& SQ = A.seq[s];
-    int sp = lsplit - SQ.split_base;
-    int sgi = 0;
-    if (sp >= SQ.seg[0].n_split) {
-        sp -= SQ.seg[0].n_split;
-        sgi = 1;
+    if (n_seq > 1) {
+        while (s + 1 < n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
+        d0 = A.seq[s].seg[0];
+        d1 = A.seq[s].seg[1];
+        seq_base = A.seq[s].split_base;
+        seq_splits = A.seq[s].n_split;
     }
-    const SegDesc& SG = SQ.seg[sgi];
-    const int r_begin = SG.row_lo + sp * A.split_rows;
-    const int r_end = min(r_begin + A.split_rows, SG.row_lo + SG.n_vis);
-    const bool single = SQ.n_split == 1;
-    const int abs_split = A.split_off + lsplit;
+    int sp = lsplit - seq_base;
+    const bool second = sp >= d0.n_split;
+    if (second) sp -= d0.n_split;
+    SegDesc SG;
+    SG.k = second ? d1.k : d0.k;
+    SG.v = second ? d1.v : d0.v;
+    SG.stride = second ? d1.stride : d0.stride;
+    SG.row_lo = second ? d1.row_lo : d0.row_lo;
+    SG.n_vis = second ? d1.n_vis : d0.n_vis;
+    SG.n_split = second ? d1.n_split : d0.n_split;
+    SG.n_rows = second ? d1.n_rows : d0.n_rows;
+    SG.vstride = second ? d1.vstride : d0.vstride;
+    const int r_begin = SG.row_lo + sp * split_rows;
+    const int r_end = min(r_begin + split_rows, SG.row_lo + SG.n_vis);
+    const bool single = seq_splits == 1;
+    const int abs_split = split_off + lsplit;
     if (wave & 1)
         slice_body<D, G, VT, QS, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
                                 s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
@@ -645,17 +676,29 @@ __global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs
     __shared__ float s_o[NWV][64][33];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // As in the decode kernel: the arguments at fixed offsets (the first
+    // sequence's split count and base, the partial and output pointers) in one
+    // round trip before anything depends on them.
+    int32_t S = A.seq[0].n_split, base = A.seq[0].split_base;
+    const int32_t split_off = A.split_off;
+    const float* const ppm = A.pm;
+    const float* const ppl = A.pl;
+    const float* const ppo = A.po;
+    asm volatile("" ::"s"(S), "s"(base), "s"(split_off), "s"(n_head_q), "s"(ppm), "s"(ppl), "s"(ppo));
+    asm volatile("" ::"s"(A.out), "s"(A.part_o), "s"(A.part_m), "s"(A.part_l));
     const int hq = blockIdx.x % n_head_q;
     const int s = blockIdx.x / n_head_q;
-    const SeqDesc& SQ = A.seq[s];
-    const int S = SQ.n_split;
+    if (s > 0) {
+        S = A.seq[s].n_split;
+        base = A.seq[s].split_base;
+    }
     if (S <= 1) return;  // written directly by the decode kernel
-    const int first = A.split_off + SQ.split_base;
+    const int first = split_off + base;
     auto load = [&](int k, float& pm, float& pl, float4 (&v)[8]) {
         const size_t pi = (size_t)(first + k) * n_head_q + hq;
-        pm = A.pm[pi];
-        pl = A.pl[pi];
-        const float4* po = (const float4*)(A.po + pi * D + 32 * wave);
+        pm = ppm[pi];
+        pl = ppl[pi];
+        const float4* po = (const float4*)(ppo + pi * D + 32 * wave);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = po[j];
     };
