@@ -21,6 +21,10 @@ ARCH = "gfx950"
 CODE_OBJECT = ["-mcode-object-version=5"]  # loadable by the ROCm 7.0 runtime torch ships
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The kernels' leading scalar arguments go into SGPRs at wave launch (up to the
+# 14 user SGPRs left for them); the code object keeps a prologue that loads
+# them from memory where the firmware does not preload.
+KERNARG_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 HIP_SOURCES = ["kvd_attend.hip"]
 HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp"]
 
@@ -29,7 +33,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += ["--offload-arch=" + ARCH] + CODE_OBJECT + NO_PACKED_FP32
+        cmd += ["--offload-arch=" + ARCH] + CODE_OBJECT + NO_PACKED_FP32 + KERNARG_PRELOAD
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -263,16 +263,20 @@ __device__ inline __amdgpu_buffer_rsrc_t vtile_rsrc(const SegDesc& sg, int g, in
     return make_rsrc(sg.v + head_off, lim);
 }
 
+// One split: segment `seg` (SG: its pointers, strides, first visible row and
+// readable rows) of sequence s, KV head g, the sp-th split of the segment and
+// the lsplit-th of the launch.  The segment's visible row count and every
+// other field of A are read only after the first tile's loads are issued.
 template <int D, int G, int VT, int QS, int ODD>
-__device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int g,
-                                           const int r_begin, const int r_end, const bool single,
-                                           const int abs_split, const int wave, const int lane, uint32_t* tk,
-                                           uint32_t* tv, float* sx, float* scw, float* sq) {
+__device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int seg,
+                                           const int g, const int sp, const int lsplit, const int n_head_kv,
+                                           const int split_rows, const float* q, const int wave, const int lane,
+                                           uint32_t* tk, uint32_t* tv, float* sx, float* scw, float* sq) {
     using S_ = Slice<D, G>;
     constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
-    const int n_tiles = (r_end - r_begin + T - 1) / T;
-    const int n_head_q = A.n_head_kv * G;
-    const float* __restrict__ qg = A.q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
+    const int r_begin = SG.row_lo + sp * split_rows;
+    const int n_head_q = n_head_kv * G;
+    const float* __restrict__ qg = q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
 
     constexpr int VW = VWin<VT>::W;
     // Unit 64 i + lane of a 9-dword window tile is row 7 i + (lane + i) / 9,
@@ -334,6 +338,23 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     uint32_t rk[9], rv[VW];
     load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
     load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, r_begin), voffv);
+    // The arguments that were not preloaded, read (and waited for) while the
+    // first tile is in flight.
+    const int32_t n_vis = A.seq[s].seg[seg].n_vis, seq_splits = A.seq[s].n_split, split_off = A.split_off;
+    const float scale_log2e = A.scale_log2e;
+    float* const out = A.out;
+    float* const po = A.po;
+    float* const pm = A.pm;
+    float* const pl = A.pl;
+    float* const part_o = A.part_o;
+    float* const part_m = A.part_m;
+    float* const part_l = A.part_l;
+    asm volatile("" ::"s"(n_vis), "s"(seq_splits), "s"(split_off), "s"(scale_log2e));
+    asm volatile("" ::"s"(out), "s"(po), "s"(pm), "s"(pl), "s"(part_o), "s"(part_m), "s"(part_l));
+    const int r_end = min(r_begin + split_rows, SG.row_lo + n_vis);
+    const int n_tiles = (r_end - r_begin + T - 1) / T;
+    const bool single = seq_splits == 1;
+    const int abs_split = split_off + lsplit;
     if (!QS && lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
     store_win(rk, tk, lane);
 
@@ -413,7 +434,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             float a = sxt[h * 64 + lane];
 #pragma unroll
             for (int b = 1; b < NB; ++b) a += sxt[(b * G + h) * 64 + lane];
-            sc[h] = (lane < nv) ? a * A.scale_log2e : -INFINITY;
+            sc[h] = (lane < nv) ? a * scale_log2e : -INFINITY;
         }
         {
             // first tile: start from the score of its first row (always visible)
@@ -519,16 +540,16 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
     if (slot == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if (single && A.part_o) {
-                *(float4*)&A.part_o[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
+            if (single && part_o) {
+                *(float4*)&part_o[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
                     make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
             } else if (single) {
                 const float inv = 1.f / l[h];
-                *(float4*)&A.out[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
+                *(float4*)&out[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
                     make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
             } else {
                 const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-                *(float4*)&A.po[pi * D + dim0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+                *(float4*)&po[pi * D + dim0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
             }
         }
     }
@@ -537,19 +558,30 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
         for (int h = 0; h < G; ++h) {
             if (!single) {
                 const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-                A.pm[pi] = m[h];
-                A.pl[pi] = l[h];
-            } else if (A.part_o) {
+                pm[pi] = m[h];
+                pl[pi] = l[h];
+            } else if (part_o) {
                 const size_t sh = (size_t)s * n_head_q + hq0 + h;
-                A.part_m[sh] = m[h];
-                A.part_l[sh] = l[h];
+                part_m[sh] = m[h];
+                part_l[sh] = l[h];
             }
         }
     }
 }
 
+// The leading arguments (14 dwords: the counts, the query and the first
+// sequence's first segment) are preloaded into SGPRs when the waves start (the
+// file is built with kernel-argument preloading), so the first split segment
+// of a one-sequence launch issues its query and K/V loads without reading its
+// arguments from memory: they sit in memory that the step's K/V stream has
+// evicted from every cache since the layer's previous call.  Everything else
+// comes from the LaunchArgs block, read while the first tile is in flight.
+// kv_seq packs n_head_kv (low 16 bits) and the launch's sequence count.
 template <int D, int G, int VT, int QS>
-__global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A) {
+__global__ void __launch_bounds__(64 * (D / 32))
+slice_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_rows, const int32_t n_split0,
+             const float* q, const uint8_t* k0, const uint8_t* v0, const int32_t stride0, const int32_t vstride0,
+             const int32_t row_lo0, const int32_t n_rows0, const LaunchArgs A) {
     using S_ = Slice<D, G>;
     constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
     __shared__ __attribute__((aligned(16))) uint32_t s_kv[NB][2][T * 9];
@@ -559,62 +591,46 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Every argument at a fixed offset -- the counts, the output pointers and
-    // the first sequence's descriptors -- is read first and waited for once.
-    // The empty asm statements (after all the reads) keep the compiler from
-    // sinking these loads below the branches that use them, which costs a
-    // round trip to the arguments per branch level; a launch of one sequence
-    // then issues its first K/V loads after a single round trip (4096 rows:
-    // 11.9 us per call instead of 12.5).
-    SegDesc d0 = A.seq[0].seg[0], d1 = A.seq[0].seg[1];
-    int32_t seq_base = 0, seq_splits = A.seq[0].n_split;
-    const int32_t n_items = A.n_items, n_head_kv = A.n_head_kv, n_seq = A.n_seq;
-    const int32_t split_rows = A.split_rows, split_off = A.split_off;
-    const float scale = A.scale_log2e;
-    const float* const q = A.q;
-    float* const ptr[8] = {A.out, A.po, A.pm, A.pl, A.part_o, A.part_m, A.part_l, nullptr};
-    const int nblk = gridDim.x;
-    asm volatile("" ::"s"(d0.k), "s"(d0.v), "s"(d0.stride), "s"(d0.row_lo), "s"(d0.n_vis), "s"(d0.n_split),
-                 "s"(d0.n_rows), "s"(d0.vstride));
-    asm volatile("" ::"s"(d1.k), "s"(d1.v), "s"(d1.stride), "s"(d1.row_lo), "s"(d1.n_vis), "s"(d1.n_rows),
-                 "s"(d1.vstride), "s"(seq_splits));
-    asm volatile("" ::"s"(n_items), "s"(n_head_kv), "s"(n_seq), "s"(split_rows), "s"(split_off), "s"(scale),
-                 "s"(q), "s"(nblk));
-    asm volatile("" ::"s"(ptr[0]), "s"(ptr[1]), "s"(ptr[2]), "s"(ptr[3]), "s"(ptr[4]), "s"(ptr[5]), "s"(ptr[6]));
-    const int item = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+    const int n_head_kv = kv_seq & 0xffff, n_seq = kv_seq >> 16;
+    // the grid is n_items rounded up to a multiple of 8 (one run per XCD)
+    const int item = (blockIdx.x & 7) * ((n_items + 7) >> 3) + (blockIdx.x >> 3);
     if (item >= n_items) return;
     const int lsplit = item / n_head_kv;
     const int g = item - lsplit * n_head_kv;
-    int s = 0;
-    if (n_seq > 1) {
-        while (s + 1 < n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
-        d0 = A.seq[s].seg[0];
-        d1 = A.seq[s].seg[1];
-        seq_base = A.seq[s].split_base;
-        seq_splits = A.seq[s].n_split;
-    }
-    int sp = lsplit - seq_base;
-    const bool second = sp >= d0.n_split;
-    if (second) sp -= d0.n_split;
+    int s = 0, sp = lsplit, seg = 0;
     SegDesc SG;
-    SG.k = second ? d1.k : d0.k;
-    SG.v = second ? d1.v : d0.v;
-    SG.stride = second ? d1.stride : d0.stride;
-    SG.row_lo = second ? d1.row_lo : d0.row_lo;
-    SG.n_vis = second ? d1.n_vis : d0.n_vis;
-    SG.n_split = second ? d1.n_split : d0.n_split;
-    SG.n_rows = second ? d1.n_rows : d0.n_rows;
-    SG.vstride = second ? d1.vstride : d0.vstride;
-    const int r_begin = SG.row_lo + sp * split_rows;
-    const int r_end = min(r_begin + split_rows, SG.row_lo + SG.n_vis);
-    const bool single = seq_splits == 1;
-    const int abs_split = split_off + lsplit;
+    SG.k = k0;
+    SG.v = v0;
+    SG.stride = stride0;
+    SG.vstride = vstride0;
+    SG.row_lo = row_lo0;
+    SG.n_rows = n_rows0;
+    if (n_seq > 1 || lsplit >= n_split0) {
+        // another sequence or the second segment: its descriptor from the block
+        while (s + 1 < n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
+        sp = lsplit - A.seq[s].split_base;
+        const int n0 = A.seq[s].seg[0].n_split;
+        if (sp >= n0) {
+            sp -= n0;
+            seg = 1;
+        }
+        const SegDesc& d = A.seq[s].seg[seg];
+        SG.k = d.k;
+        SG.v = d.v;
+        SG.stride = d.stride;
+        SG.vstride = d.vstride;
+        SG.row_lo = d.row_lo;
+        SG.n_rows = d.n_rows;
+        // wait here, so that the one-sequence path meets no pending load
+        asm volatile("" ::"s"(SG.k), "s"(SG.v), "s"(SG.stride), "s"(SG.vstride), "s"(SG.row_lo), "s"(SG.n_rows));
+    }
+    SG.n_vis = SG.n_split = 0;  // not used: slice_body reads the visible row count itself
     if (wave & 1)
-        slice_body<D, G, VT, QS, 1>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                                s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
+        slice_body<D, G, VT, QS, 1>(A, SG, s, seg, g, sp, lsplit, n_head_kv, split_rows, q, wave, lane,
+                                    s_kv[wave][0], s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
     else
-        slice_body<D, G, VT, QS, 0>(A, SG, s, g, r_begin, r_end, single, abs_split, wave, lane, s_kv[wave][0],
-                                s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
+        slice_body<D, G, VT, QS, 0>(A, SG, s, seg, g, sp, lsplit, n_head_kv, split_rows, q, wave, lane,
+                                    s_kv[wave][0], s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
 }
 
 // Merge n partial results (m_k, l_k, o_k) of one (sequence, query head) in
@@ -622,11 +638,13 @@ __global__ void __launch_bounds__(64 * (D / 32)) slice_kernel(const LaunchArgs A
 // Every lane loads its partial's maximum, sum and 32 outputs together (one
 // round trip), the weights follow from a wave maximum, and the 64 weighted
 // rows are summed column by column through LDS in index order, so the result
-// does not depend on timing.  `load(k, m, l, v)` fetches partial k (k < n).
+// does not depend on timing.  `load(k, m, l, v)` fetches partial k (k < n);
+// `after_first_load()` runs once the first 64 partials are requested.
 // Returns, in lanes 0..31, dimension 32 * wave + lane of O = sum e^(m_k - M) o_k,
 // with M and L = sum e^(m_k - M) l_k in every lane.
-template <class Load>
-__device__ inline void merge_rows(const Load& load, int n, int lane, float (*so)[33], float& O, float& M, float& L) {
+template <class Load, class Hook>
+__device__ inline void merge_rows(const Load& load, const Hook& after_first_load, int n, int lane, float (*so)[33],
+                                  float& O, float& M, float& L) {
     M = -INFINITY;
     L = 0.f;
     O = 0.f;
@@ -636,6 +654,7 @@ __device__ inline void merge_rows(const Load& load, int n, int lane, float (*so)
         float pm, pl;
         float4 v[8];
         load(ok ? k : c0, pm, pl, v);
+        if (c0 == 0) after_first_load();
         pm = ok ? pm : -INFINITY;
         pl = ok ? pl : 0.f;
         const float Mn = fmaxf(M, wave_max(pm));
@@ -670,24 +689,20 @@ __device__ inline void merge_rows(const Load& load, int n, int lane, float (*so)
 // (sequence, query head), one wave per 32 dims.  A separate launch, so the
 // partials written by the decode kernel are visible without cache
 // maintenance inside a kernel.
+// Leading arguments preloaded into SGPRs as in the decode kernel: the first
+// sequence's split count and the partials, so the partial loads of a
+// one-sequence launch start without reading its arguments from memory.
 template <int D>
-__global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs A, int32_t n_head_q) {
+__global__ void __launch_bounds__(64 * (D / 32))
+combine_kernel(const int32_t n_head_q, const int32_t split_off, const int32_t n_split0, const float* ppm,
+               const float* ppl, const float* ppo, const LaunchArgs A) {
     constexpr int NWV = D / 32;
     __shared__ float s_o[NWV][64][33];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // As in the decode kernel: the arguments at fixed offsets (the first
-    // sequence's split count and base, the partial and output pointers) in one
-    // round trip before anything depends on them.
-    int32_t S = A.seq[0].n_split, base = A.seq[0].split_base;
-    const int32_t split_off = A.split_off;
-    const float* const ppm = A.pm;
-    const float* const ppl = A.pl;
-    const float* const ppo = A.po;
-    asm volatile("" ::"s"(S), "s"(base), "s"(split_off), "s"(n_head_q), "s"(ppm), "s"(ppl), "s"(ppo));
-    asm volatile("" ::"s"(A.out), "s"(A.part_o), "s"(A.part_m), "s"(A.part_l));
     const int hq = blockIdx.x % n_head_q;
     const int s = blockIdx.x / n_head_q;
+    int32_t S = n_split0, base = 0;  // sequence 0 starts the launch's splits
     if (s > 0) {
         S = A.seq[s].n_split;
         base = A.seq[s].split_base;
@@ -702,8 +717,10 @@ __global__ void __launch_bounds__(64 * (D / 32)) combine_kernel(const LaunchArgs
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = po[j];
     };
+    // the output pointers, read while the first partials are in flight
+    auto read_outputs = [&]() { asm volatile("" ::"s"(A.out), "s"(A.part_o), "s"(A.part_m), "s"(A.part_l)); };
     float O, M, L;
-    merge_rows(load, S, lane, s_o[wave], O, M, L);
+    merge_rows(load, read_outputs, S, lane, s_o[wave], O, M, L);
     if (lane < 32) write_final(A, D, (size_t)s * n_head_q + hq, 32 * wave + lane, O, M, L, wave == 0 && lane == 0);
 }
 
@@ -728,12 +745,13 @@ __global__ void __launch_bounds__(64 * (D / 32)) merge_kernel(const float* parts
         for (int j = 0; j < 8; ++j) v[j] = po[j];
     };
     float O, M, L;
-    merge_rows(load, n_part, lane, s_o[wave], O, M, L);
+    merge_rows(load, [] {}, n_part, lane, s_o[wave], O, M, L);
     if (lane < 32) out[sh * D + 32 * wave + lane] = O / L;
 }
 
-typedef void (*decode_fn)(const LaunchArgs);
-typedef void (*combine_fn)(const LaunchArgs, int32_t);
+typedef void (*decode_fn)(int32_t, int32_t, int32_t, int32_t, const float*, const uint8_t*, const uint8_t*, int32_t,
+                          int32_t, int32_t, int32_t, const LaunchArgs);
+typedef void (*combine_fn)(int32_t, int32_t, int32_t, const float*, const float*, const float*, const LaunchArgs);
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
@@ -860,15 +878,18 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         L.n_items = (int32_t)(nsplit * a->n_head_kv);
         L.split_off = (int32_t)base0;
         L.scale_log2e = scale_log2e;
-        const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);
-        hipLaunchKernelGGL(dk, dim3(grid), dim3(64 * p.waves), 0, (hipStream_t)stream, L);
+        const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);  // the kernel assumes this rounding
+        const SegDesc& f = L.seq[0].seg[0];
+        hipLaunchKernelGGL(dk, dim3(grid), dim3(64 * p.waves), 0, (hipStream_t)stream, L.n_items,
+                           L.n_head_kv | (L.n_seq << 16), L.split_rows, f.n_split, L.q, f.k, f.v, f.stride, f.vstride,
+                           f.row_lo, f.n_rows, L);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(KVD_EHIP, "decode kernel launch: %s", hipGetErrorString(e));
         bool multi = false;
         for (int j = 0; j < ns; ++j) multi |= L.seq[j].n_split > 1;
         if (multi) {
-            hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q)), dim3(2 * D), 0, (hipStream_t)stream, L,
-                               (int32_t)n_head_q);
+            hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q)), dim3(2 * D), 0, (hipStream_t)stream,
+                               (int32_t)n_head_q, L.split_off, L.seq[0].n_split, L.pm, L.pl, L.po, L);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(KVD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
         }
