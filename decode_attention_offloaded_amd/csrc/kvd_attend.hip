@@ -16,7 +16,10 @@
 // block's 32 dims for all G query heads (one lane per row; the query chunks
 // from LDS or, once several workgroups share a CU, from SGPRs), the D / 32
 // block partials meet in LDS at one barrier per tile, every wave runs the same
-// online softmax, and wave w accumulates the values of its 32 dims.
+// online softmax, and wave w accumulates the values of its 32 dims.  The
+// arguments a split needs before its first loads are kernel arguments that the
+// hardware preloads into SGPRs; the rest are read while the first tile is in
+// flight.
 // A split with siblings writes an unnormalised partial (m, l, o) to the
 // workspace and a second, small launch merges the partials of each
 // (sequence, query head) in split order, so the result depends only on the
@@ -28,7 +31,6 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
-
 
 #include "kvd_internal.h"
 #include "kvd_plan.h"
