@@ -270,7 +270,7 @@ def tiled(args, torch, kvd, inputs, link):
     from decode_attention_offloaded_amd import tiled as tl
     c = inputs.config(3)
     res = tl.run_tiled(torch, kvd, inputs, c, n_layers=args.tiled_layers, depths=(0, 1), budget_bytes=128 << 20,
-                       tokens=args.tiled_tokens, warmup=1, log=log, distinct_layers=4)
+                       tokens=args.tiled_tokens, warmup=2, log=log, distinct_layers=4)
     res.pop("outs", None)
     peak = max(link.values())
     res["link_peak_GBps"] = peak
@@ -328,7 +328,7 @@ def residency(args, torch, kvd, inputs, link):
         if ring_k is not None:
             arms.append(("%dGiB_ring+%d" % (gib, ring_k), 1, budget, ring_k))
         arms.append(("%dGiB_ordered+%d" % (gib, ord_k), 0, 0, ord_k))
-    res = stack.run_residency(torch, kvd, inputs, c, arms, n_layers=L, tokens=args.residency_tokens, warmup=1,
+    res = stack.run_residency(torch, kvd, inputs, c, arms, n_layers=L, tokens=args.residency_tokens, warmup=2,
                               log=log, distinct_layers=4)
     res["compute_ms_per_layer"] = round(cms, 4)
     res["link_peak_GBps"] = peak
@@ -409,11 +409,11 @@ def head_split(args, torch, kvd, inputs, link):
     L = args.residency_layers
     peak = max(link.values())
     hs = headsplit.run_headsplit(torch, kvd, inputs, c, 3, n_layers=L, depths=(0, 1), budget_bytes=1 << 30,
-                                 tokens=args.residency_tokens, warmup=1, log=log, distinct_layers=4)
+                                 tokens=args.residency_tokens, warmup=2, log=log, distinct_layers=4)
     k_layers = L * 3 // 8
     ls = stack.run_residency(torch, kvd, inputs, c, [("ring+%d" % k_layers, 1, 1 << 30, k_layers),
                                                      ("ordered+%d" % k_layers, 0, 0, k_layers)],
-                             n_layers=L, tokens=args.residency_tokens, warmup=1, log=log, distinct_layers=4)
+                             n_layers=L, tokens=args.residency_tokens, warmup=2, log=log, distinct_layers=4)
     for arm in hs["arms"].values():
         arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
     log("head split 3/8: %s; layer split %d/%d: %s" % (
@@ -429,7 +429,7 @@ def long_context(args, torch, kvd, inputs):
     out = {}
     for budget_mib in (128, 1024):
         r = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1, 2),
-                                    budget_bytes=budget_mib << 20, tokens=args.long_tokens, warmup=1, log=log,
+                                    budget_bytes=budget_mib << 20, tokens=args.long_tokens, warmup=2, log=log,
                                     distinct_layers=4)
         out[str(budget_mib)] = r
         log("long context, budget %d MiB: %s" % (budget_mib, {k: (v["ms_per_token"], v["declined"])
@@ -642,21 +642,21 @@ def main():
     ap.add_argument("--curve", type=int, default=1)
     ap.add_argument("--pipeline", type=int, default=1)
     ap.add_argument("--pipe-layers", type=int, default=64)
-    ap.add_argument("--pipe-tokens", type=int, default=8)
+    ap.add_argument("--pipe-tokens", type=int, default=20)
     ap.add_argument("--cpu-baseline", type=int, default=1)
     ap.add_argument("--batched", type=int, default=1, help="run the 16-sequence mixed-residency stack")
     ap.add_argument("--batched-layers", type=int, default=64)
     ap.add_argument("--batched-tokens", type=int, default=4)
     ap.add_argument("--tiled", type=int, default=1, help="run 131072 rows at 128 MiB in ring-streamed tiles")
     ap.add_argument("--tiled-layers", type=int, default=64)
-    ap.add_argument("--tiled-tokens", type=int, default=3)
+    ap.add_argument("--tiled-tokens", type=int, default=5)
     ap.add_argument("--residency", type=int, default=1, help="run the 131072-row residency-planner arms")
     ap.add_argument("--residency-layers", type=int, default=64)
-    ap.add_argument("--residency-tokens", type=int, default=3)
+    ap.add_argument("--residency-tokens", type=int, default=5)
     ap.add_argument("--asym", type=int, default=1, help="run the q8_0 K / q4_0 V legs")
     ap.add_argument("--headsplit", type=int, default=1, help="run the per-head residency split leg")
     ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
-    ap.add_argument("--long-tokens", type=int, default=3)
+    ap.add_argument("--long-tokens", type=int, default=5)
     ap.add_argument("--cpu-extra", type=int, default=0,
                     help="also time the oracle single-threaded and on the 16384/131072-row and batched layers")
     args = ap.parse_args()
