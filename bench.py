@@ -19,6 +19,7 @@ Default run (one JSON line on stdout):
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
 import sys
@@ -229,6 +230,42 @@ def link_peak(torch):
     return res
 
 
+def link_environment(torch):
+    """Where the link figures come from: the GPU's PCI address and NUMA node,
+    the NUMA nodes of the CPUs this process may run on (pinned buffers are
+    allocated from them), and whether HIP's host-to-device copies use the SDMA
+    engines (HSA_ENABLE_SDMA unset or not 0).  Fields that the system does not
+    expose are None."""
+    info = {"gpu_pci": None, "gpu_numa_node": None, "process_numa_nodes": None}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        bdf = "%04x:%02x:%02x.0" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        info["gpu_pci"] = bdf
+        with open("/sys/bus/pci/devices/%s/numa_node" % bdf) as f:
+            info["gpu_numa_node"] = int(f.read().strip())
+    except (OSError, ValueError, AttributeError):
+        pass
+    try:
+        cpus = os.sched_getaffinity(0)
+        nodes = set()
+        for path in glob.glob("/sys/devices/system/node/node*/cpulist"):
+            node = int(path.split("/node")[-1].split("/")[0])
+            with open(path) as f:
+                for part in f.read().strip().split(","):
+                    if not part:
+                        continue
+                    lo, _, hi = part.partition("-")
+                    if cpus & set(range(int(lo), int(hi or lo) + 1)):
+                        nodes.add(node)
+        info["process_numa_nodes"] = sorted(nodes) or None
+    except (OSError, ValueError):
+        pass
+    sdma = os.environ.get("HSA_ENABLE_SDMA")
+    info["HSA_ENABLE_SDMA"] = sdma
+    info["sdma_copies"] = sdma is None or sdma != "0"
+    return info
+
+
 def pipeline(args, torch, kvd, inputs, link):
     """Host-resident 64-layer stack at 16384 rows: ordered (depth 0) vs pipelined
     (depth 1, 128 MiB ring), against the pinned H2D link peak measured here."""
@@ -240,6 +277,7 @@ def pipeline(args, torch, kvd, inputs, link):
                                   budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log)
     res["link_GBps_by_MiB"] = link
     res["link_peak_GBps"] = peak
+    res["link_environment"] = link_environment(torch)
     for arm in res["arms"].values():
         arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
     return res
