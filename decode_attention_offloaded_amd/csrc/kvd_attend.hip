@@ -410,8 +410,13 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
 #pragma unroll
                     for (int h = 0; h < G; ++h) qc[h] = *(const float4*)&sq[h * 32 + off];
                 }
-                const uint32_t x = ODD ? w[c + 1] : __builtin_amdgcn_alignbyte(w[c + 1], w[c], 2);
-                const float k0 = sbyte(x, 0), k1 = sbyte(x, 1), k2 = sbyte(x, 2), k3 = sbyte(x, 3);
+                // codes 4c .. 4c+3: bytes 0..3 of dword c+1 of an odd block's
+                // window; bytes 2, 3 of dword c and 0, 1 of dword c+1 of an even
+                // block's (its codes start at byte 2), each converted from its byte
+                const float k0 = ODD ? sbyte(w[c + 1], 0) : sbyte(w[c], 2);
+                const float k1 = ODD ? sbyte(w[c + 1], 1) : sbyte(w[c], 3);
+                const float k2 = ODD ? sbyte(w[c + 1], 2) : sbyte(w[c + 1], 0);
+                const float k3 = ODD ? sbyte(w[c + 1], 3) : sbyte(w[c + 1], 1);
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     dot[h] = fmaf(qc[h].x, k0, dot[h]);
@@ -420,7 +425,8 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
                     dot[h] = fmaf(qc[h].w, k3, dot[h]);
                 }
             }
-            const float dk = ODD ? half_hi(w[0]) : half_lo(w[0]);
+            // block scale times the softmax scale (exp2 domain)
+            const float dk = (ODD ? half_hi(w[0]) : half_lo(w[0])) * scale_log2e;
 #pragma unroll
             for (int h = 0; h < G; ++h) sxt[(wave * G + h) * 64 + lane] = dot[h] * dk;
         }
@@ -436,7 +442,12 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             float a = sxt[h * 64 + lane];
 #pragma unroll
             for (int b = 1; b < NB; ++b) a += sxt[(b * G + h) * 64 + lane];
-            sc[h] = (lane < nv) ? a * scale_log2e : -INFINITY;
+            sc[h] = a;
+        }
+        if (nv < T) {
+            // only a split's last tile can be partial
+#pragma unroll
+            for (int h = 0; h < G; ++h) sc[h] = (lane < nv) ? sc[h] : -INFINITY;
         }
         {
             // first tile: start from the score of its first row (always visible)
@@ -487,10 +498,16 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
 #pragma unroll 4
         for (int ps = 0; ps < 8; ++ps) {
             const int r = ps * 8 + slot;
-            uint32_t x;
+            uint32_t x = 0;
+            float vq[4];
             if constexpr (VT == 0) {
+                // dims 4 grp .. 4 grp + 3, bytes picked as for the scores
                 const uint32_t* rp = tv + r * 9;
-                x = ODD ? rp[grp + 1] : __builtin_amdgcn_alignbyte(rp[grp + 1], rp[grp], 2);
+                const uint32_t lo = rp[grp], hi = rp[grp + 1];
+                vq[0] = ODD ? sbyte(hi, 0) : sbyte(lo, 2);
+                vq[1] = ODD ? sbyte(hi, 1) : sbyte(lo, 3);
+                vq[2] = ODD ? sbyte(hi, 2) : sbyte(hi, 0);
+                vq[3] = ODD ? sbyte(hi, 3) : sbyte(hi, 1);
             } else {
                 // dims 4 grp .. 4 grp + 3: low nibbles of code bytes 4 grp .. (grp < 4),
                 // high nibbles of bytes 4 (grp - 4) .. (grp >= 4)
@@ -510,7 +527,7 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float vv = VT ? (float)((x >> (8 * e)) & 0xFFu) : sbyte(x, e);
+                const float vv = VT ? (float)((x >> (8 * e)) & 0xFFu) : vq[e];
 #pragma unroll
                 for (int h = 0; h < G; ++h) o[h][e] = fmaf(c[h], vv, o[h][e]);
             }
