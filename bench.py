@@ -728,7 +728,7 @@ def main():
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "slice_kernel<128,5,0,0> + combine_kernel<128> (one call)",
+                     "kernel": "decode_kernel<128,5,0,1> + combine_kernel<128> (one call)",
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
         "hbm_stream_ceiling": hbm_stream_ceiling(torch),

@@ -10,16 +10,15 @@
 // merged by their running maxima and sums).
 //
 // Shape of the work.  A split = one (sequence, KV head, row range) = one
-// workgroup of D / 32 waves, wave w owning q8_0 block w (dims 32w .. 32w + 31)
-// of every row.  All waves walk the same 64-row tiles: each loads a 36-byte
-// window around its block (K and V, one tile ahead in registers), scores its
-// block's 32 dims for all G query heads (one lane per row; the query chunks
-// from LDS or, once several workgroups share a CU, from SGPRs), the D / 32
-// block partials meet in LDS at one barrier per tile, every wave runs the same
-// online softmax, and wave w accumulates the values of its 32 dims.  The
-// arguments a split needs before its first loads are kernel arguments that the
-// hardware preloads into SGPRs; the rest are read while the first tile is in
-// flight.
+// workgroup of four waves.  Each wave walks its own sub-tiles of the split's
+// rows (every fourth one) over all head_dim dims of the head and keeps its own
+// online-softmax state; the four states meet in LDS once, at the end of the
+// split.  Inside a wave, lane 16 r + i works on q8_0 block r % (D / 32) of one
+// row; the query and the softmax weights reach the lanes that need them through
+// DPP row broadcasts folded into the multiply-adds (details at decode_kernel).
+// The arguments a split needs before its first loads are kernel arguments that
+// the hardware preloads into SGPRs; the rest are read while the first sub-tile
+// is in flight.
 // A split with siblings writes an unnormalised partial (m, l, o) to the
 // workspace and a second, small launch merges the partials of each
 // (sequence, query head) in split order, so the result depends only on the
@@ -32,14 +31,13 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kvd_internal.h"
 #include "kvd_plan.h"
 
 namespace kvd {
 namespace {
-
-// Constant address space: loads through it are scalar (s_load) when uniform.
-typedef const float __attribute__((address_space(4)))* const_f32_ptr;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 
@@ -153,440 +151,295 @@ __device__ inline float half_lo(uint32_t w) {
     return (float)h;
 }
 
-__device__ inline float half_hi(uint32_t w) {
-    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-    return (float)h;
-}
-
-__device__ inline float4 ldq4(const_f32_ptr p) { return make_float4(p[0], p[1], p[2], p[3]); }
-
-__device__ inline float sbyte(uint32_t w, int e) { return (float)(int8_t)(w >> (8 * e)); }
-
-template <int D>
-struct Geo {
-    static constexpr int NB = D / 32;   // q8_0 blocks per head
-    static constexpr int CB = 34 * NB;  // bytes of one head of one row
-};
-
-// Buffer descriptor for head g of the 64-row tile starting at row0 of one
-// tensor (K or V).  Its range ends with head g's chunk in the last readable
-// row, so loads past the segment return zeros instead of touching memory.
-template <int D>
-__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, const SegDesc& sg, int g, int row0) {
-    using G_ = Geo<D>;
-    const int64_t head_off = (int64_t)row0 * sg.stride + (int64_t)g * G_::CB;
-    const int64_t lim64 = (int64_t)(sg.n_rows - 1 - row0) * sg.stride + G_::CB;
-    const int32_t lim = (int32_t)(lim64 > 0x7fffffff ? 0x7fffffff : lim64);
-    return make_rsrc(base + head_off, lim);
-}
-
 // ---------------------------------------------------------------------------
-// The decode kernel.  A workgroup has one wave per q8_0 block of the head
-// (D / 32 waves) and walks the split's rows in 64-row tiles, all waves on the
-// same tile:
-//   * wave w loads only block w of each row (a 9-dword window around its 34
-//     bytes) for K and V, one tile ahead in registers, staged through a
-//     wave-private LDS tile;
-//   * scores: one lane per row, the block's 32 codes against the query slice
-//     (read 4 dims x G heads at a time, from LDS or SGPRs), times the block
-//     scale; the D / 32 block partials meet in LDS at one workgroup barrier
-//     per tile (LDS-only fences, so the prefetch stays in flight), and every
-//     wave sums them in the same order, so all waves hold identical scores;
-//   * online softmax, repeated identically in each wave: the running maximum
-//     is only raised when a score passes it by more than kLazyMax (log2
-//     units), so most tiles need no wave-wide maximum and no rescale;
-//   * values: wave w accumulates the 32 dims of block w; a lane holds 4 dims
-//     (G x 4 accumulators) and 8 consecutive lanes take 8 rows of a pass;
-//   * at the end each wave folds its 8 row slots (three DPP steps) and writes
-//     its 32 dims: the waves own disjoint dims, so no cross-wave merge.
+// The decode kernel.  A workgroup (four waves) takes one split: one
+// (sequence, KV head, row range).  The waves walk the split's rows in
+// sub-tiles of R rows, wave w taking sub-tiles w, w + 4, w + 8, ..., and each
+// keeps its own online-softmax state; the four states are merged through LDS
+// once, at the end of the split.  There is no barrier inside the row loop.
+//
+// Lanes.  A wave's 64 lanes are four DPP rows of 16.  Lane 16 dr + i works on
+// q8_0 block b = dr % NB of the head (dims 32 b .. 32 b + 31) and on row
+// 16 (dr / NB) + i of the sub-tile, so R = 16 * 4 / NB rows (16 at head_dim
+// 128, 32 at 64).
+//   * Scores: a lane converts the 32 codes of its (row, block) and multiplies
+//     them with the query; the query value for code j of block b sits in lane
+//     j % 16 of the DPP row (register j / 16) and reaches every lane of the row
+//     through a DPP row broadcast folded into the FMA (v_fmac_f32_dpp
+//     row_newbcast), so a lane holds 2 G query floats instead of 32 G.  The
+//     block partials of a row meet through two lane exchanges (ds_swizzle and
+//     ds_bpermute, no LDS memory) in the same order in every lane.
+//   * Softmax: every lane of a row holds the row's scores; the running maximum
+//     of each head is wave-uniform and is raised only when a score passes it
+//     by more than kLazyMax (log2 units), so most sub-tiles need no wave-wide
+//     maximum and no rescale.  A lane's weight p times its block's V scale is
+//     the coefficient c of that (row, block).
+//   * Values: the 16 lanes of a DPP row take two dims each of the row's block
+//     (q8_0: dims 2i, 2i + 1; q4_0: dims i, i + 16), and loop over the 16 rows
+//     of their row set; the coefficient of row n comes from lane n of the same
+//     DPP row by the same broadcast, so a lane keeps 2 G accumulators.
+// Loads: a sub-tile of one KV head is R rows x 34 NB bytes (2176 bytes of K at
+// either head size), read as 9 dword loads per lane over consecutive units of
+// the sub-tile (one or two rows per instruction) and copied to a wave-private
+// LDS tile in the same order; the next sub-tile is in flight in registers
+// while this one is computed.
 constexpr float kLazyMax = 8.0f;
 
-// First dword of the 9-dword window holding block b of a head chunk, and the
-// byte offset of the block's scale within that window (0 or 2).
-__device__ inline int win_dword(int b) { return (34 * b) >> 2; }
+// v_fmac_f32 with its first source taken from lane N of the lane's DPP row
+// (row_newbcast, gfx90a and later).  Written as inline assembly because the
+// compiler does not fold a DPP move into a multiply-add; the source must not
+// be written by a VALU instruction in the two instructions before (the callers
+// separate such writes with kvd::dpp_source_guard).
+template <int N>
+__device__ __forceinline__ void fmac_bc(float& acc, float src, float x);
+#define KVD_FMAC_BC(N)                                                                                       \
+    template <>                                                                                              \
+    __device__ __forceinline__ void fmac_bc<N>(float& acc, float src, float x) {                            \
+        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"                       \
+            : "+v"(acc)                                                                                      \
+            : "v"(src), "v"(x));                                                                             \
+    }
+KVD_FMAC_BC(0)
+KVD_FMAC_BC(1)
+KVD_FMAC_BC(2)
+KVD_FMAC_BC(3)
+KVD_FMAC_BC(4)
+KVD_FMAC_BC(5)
+KVD_FMAC_BC(6)
+KVD_FMAC_BC(7)
+KVD_FMAC_BC(8)
+KVD_FMAC_BC(9)
+KVD_FMAC_BC(10)
+KVD_FMAC_BC(11)
+KVD_FMAC_BC(12)
+KVD_FMAC_BC(13)
+KVD_FMAC_BC(14)
+KVD_FMAC_BC(15)
+#undef KVD_FMAC_BC
 
-template <int D, int G>
-struct Slice {
-    static constexpr int NB = D / 32;        // waves per workgroup
-    static constexpr int GP = (G + 3) / 4 * 4;
-    static constexpr int T = 64;             // rows per tile
-    static constexpr int W = 9;              // dwords per row window
+// acc = (src of lane N of the DPP row) * x, the first term of a sum.
+template <int N>
+__device__ __forceinline__ void mul_bc(float& acc, float src, float x);
+#define KVD_MUL_BC(N)                                                                                        \
+    template <>                                                                                              \
+    __device__ __forceinline__ void mul_bc<N>(float& acc, float src, float x) {                             \
+        asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"                        \
+            : "=v"(acc)                                                                                      \
+            : "v"(src), "v"(x));                                                                             \
+    }
+KVD_MUL_BC(0)
+#undef KVD_MUL_BC
+
+// Two wait states after the last VALU write of the registers that the
+// following DPP broadcasts read; the registers pass through the statement so
+// the compiler keeps every such write before it.
+template <int N>
+__device__ __forceinline__ void dpp_source_guard(float (&r)[N]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));
+    asm volatile("s_nop 1" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void dpp_source_guard(float (&r)[N][2]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k][0]), "+v"(r[k][1]));
+    asm volatile("s_nop 1" ::: "memory");
+}
+
+constexpr int gcd16(int x) { return (x & 15) == 0 ? 16 : (x & 7) == 0 ? 8 : (x & 3) == 0 ? 4 : (x & 1) == 0 ? 2 : 1; }
+
+// One head of one row (CB bytes) read as whole 16-byte units: the units from
+// the 16-byte boundary at or below the chunk start, enough for the largest
+// offset the chunk can have within its unit.  UR units per row; in LDS a row
+// is P = 4 UR dwords, the chunk `lead` bytes into it.
+template <int CB>
+struct RowUnits {
+    static constexpr int LEAD_MAX = 16 - gcd16(CB);
+    static constexpr int UR = (CB + LEAD_MAX + 15) / 16;
+    static constexpr int P = 4 * UR;
 };
 
-__device__ inline void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Window loads: instruction i of 9 reads unit 64 i + lane of the tile's
-// 64 x 9 dwords (row = unit / 9, dword = unit % 9), so the LDS copy is a
-// plain lane-contiguous store and each instruction covers ~7 rows of 36
-// contiguous bytes.
-__device__ inline void load_win(uint32_t (&r)[9], __amdgpu_buffer_rsrc_t rs, const int32_t (&voff)[9]) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0);
-}
-
-__device__ inline void store_win(const uint32_t (&r)[9], uint32_t* t, int lane) {
-#pragma unroll
-    for (int i = 0; i < 9; ++i) t[64 * i + lane] = r[i];
-}
-
-// V windows: q8_0 V as K (9 dwords around the 34-byte block); q4_0 V: 5
-// dwords around the 18-byte block, 64 rows x 5 dwords = 5 loads per lane
-// (unit 64 i + lane -> row = unit / 5, dword = unit % 5).
-template <int VT>
-struct VWin {
-    static constexpr int W = VT ? 5 : 9;        // dwords per row window
-    static constexpr int BB = VT ? 18 : 34;     // bytes per block
-};
-
-template <int VW>
-__device__ inline void load_vwin(uint32_t (&r)[VW], __amdgpu_buffer_rsrc_t rs, const int32_t (&voff)[VW]) {
-#pragma unroll
-    for (int i = 0; i < VW; ++i) r[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], 0, 0);
-}
-
-template <int VW>
-__device__ inline void store_vwin(const uint32_t (&r)[VW], uint32_t* t, int lane) {
-#pragma unroll
-    for (int i = 0; i < VW; ++i) t[64 * i + lane] = r[i];
-}
-
-// Descriptor for head g of the V tile at row0 (V rows of their own stride and
-// block size); loads past the segment return zero.
 template <int D, int VT>
-__device__ inline __amdgpu_buffer_rsrc_t vtile_rsrc(const SegDesc& sg, int g, int row0) {
-    constexpr int CBV = (D / 32) * VWin<VT>::BB;
-    const int64_t head_off = (int64_t)row0 * sg.vstride + (int64_t)g * CBV;
-    const int64_t lim64 = (int64_t)(sg.n_rows - 1 - row0) * sg.vstride + CBV;
-    const int32_t lim = (int32_t)(lim64 > 0x7fffffff ? 0x7fffffff : lim64);
-    return make_rsrc(sg.v + head_off, lim);
+struct Lay {
+    static constexpr int NB = D / 32;           // q8_0 blocks per head
+    static constexpr int RSETS = 4 / NB;        // row sets per sub-tile (DPP rows per block)
+    static constexpr int R = 16 * RSETS;        // rows per sub-tile
+    static constexpr int CB = 34 * NB;          // K bytes of one head of one row
+    static constexpr int VB = VT ? 18 : 34;     // V bytes per block
+    static constexpr int CBV = VB * NB;         // V bytes of one head of one row
+    static constexpr int PK = RowUnits<CB>::P;  // LDS dwords per K row
+    static constexpr int PV = RowUnits<CBV>::P;
+    static constexpr int KUW = R * RowUnits<CB>::UR;   // 16-byte units of a K sub-tile
+    static constexpr int VUW = R * RowUnits<CBV>::UR;
+    static constexpr int KW = (KUW + 63) / 64;  // 16-byte loads per lane (K)
+    static constexpr int VW = (VUW + 63) / 64;
+    static constexpr int KN = (R * PK + 63) / 64;  // dword loads per lane (K)
+    static constexpr int VN = (R * PV + 63) / 64;
+    static_assert(4 * KW >= KN && 4 * VW >= VN, "the dword loads fit the registers of the 16-byte loads");
+    static constexpr int KT = 4 * 64 * KW;      // LDS dwords of the K tile
+    static constexpr int VT_ = 4 * 64 * VW;
+};
+
+// Per-wave LDS: the K and V sub-tile, reused at the end of the split for the
+// wave's (m, l, o) before the four waves merge.
+template <int D, int G, int VT>
+struct WaveLds {
+    using L_ = Lay<D, VT>;
+    static constexpr int K = L_::KT;
+    static constexpr int V = L_::VT_;
+    static constexpr int MERGE = G * (D + 2);
+    static constexpr int DWORDS = (K + V > MERGE ? K + V : MERGE);
+};
+
+// Descriptor for head g of the sub-tile at row0 of one tensor (rows `stride`
+// bytes apart, cb bytes per head).  It starts `lead` bytes before the head's
+// chunk and ends with the chunk of the last readable row, so loads past the
+// segment return zeros (and a sub-tile that starts past the segment reads
+// nothing).
+__device__ inline __amdgpu_buffer_rsrc_t sub_rsrc(const uint8_t* base, int32_t stride, int32_t n_rows, int cb, int g,
+                                                  int lead, int row0) {
+    const int64_t off = (int64_t)row0 * stride + (int64_t)g * cb - lead;
+    const int64_t lim64 = (int64_t)(n_rows - 1 - row0) * stride + lead + cb;
+    const int32_t lim = (int32_t)(lim64 > 0x7fffffff ? 0x7fffffff : lim64 < 0 ? 0 : lim64);
+    return make_rsrc(base + off, lim);
 }
 
-// One split: segment `seg` (SG: its pointers, strides, first visible row and
-// readable rows) of sequence s, KV head g, the sp-th split of the segment and
-// the lsplit-th of the launch.  The segment's visible row count and every
-// other field of A are read only after the first tile's loads are issued.
-template <int D, int G, int VT, int QS, int ODD>
-__device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& SG, const int s, const int seg,
-                                           const int g, const int sp, const int lsplit, const int n_head_kv,
-                                           const int split_rows, const float* q, const int wave, const int lane,
-                                           uint32_t* tk, uint32_t* tv, float* sx, float* scw, float* sq) {
-    using S_ = Slice<D, G>;
-    constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
-    const int r_begin = SG.row_lo + sp * split_rows;
-    const int n_head_q = n_head_kv * G;
-    const float* __restrict__ qg = q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * wave;
-
-    constexpr int VW = VWin<VT>::W;
-    // Unit 64 i + lane of a 9-dword window tile is row 7 i + (lane + i) / 9,
-    // dword (lane + i) % 9.  With lane = 9 r0 + d0 (d0 < 9), (lane + i) / 9 is
-    // r0 plus a carry (d0 + i >= 9), so each offset is one select and one
-    // three-way add from a per-lane base and a wave-uniform step.
-    const int r0 = (lane * 57) >> 9;  // lane / 9 for lane < 64
-    const int d0 = lane - 9 * r0;
-    int32_t voff[9];
-    {
-        const int32_t base = r0 * SG.stride + 4 * d0 + win_dword(wave) * 4;
+// Offsets of the 16-byte units u = 64 m + lane of a sub-tile (row u / UR,
+// unit u % UR); units past the sub-tile re-read its last unit (their LDS copy
+// is never read).
+template <int N, int UR, int NU>
+__device__ inline void wide_offsets(int32_t (&off)[N], int lane, int32_t stride) {
 #pragma unroll
-        for (int i = 0; i < 9; ++i)
-            voff[i] = base + i * (7 * SG.stride + 4) + (d0 + i >= 9 ? SG.stride - 36 : 0);
-    }
-    int32_t voffv[VW];
-    if constexpr (VW == 9) {
-        const int32_t base = r0 * SG.vstride + 4 * d0 + ((VWin<VT>::BB * wave) >> 2) * 4;
-#pragma unroll
-        for (int i = 0; i < 9; ++i)
-            voffv[i] = base + i * (7 * SG.vstride + 4) + (d0 + i >= 9 ? SG.vstride - 36 : 0);
-    } else {
-        const int32_t base = ((VWin<VT>::BB * wave) >> 2) * 4;
-#pragma unroll
-        for (int i = 0; i < VW; ++i) {
-            const int u = 64 * i + lane;
-            voffv[i] = (u / VW) * SG.vstride + (u % VW) * 4 + base;
-        }
-    }
-
-    // q4_0 V: o accumulates c * code over the unsigned 4-bit codes and cs the
-    // weights c, so that o - 8 * cs is the sum over c * (code - 8)
-    float m[G], l[G], o[G][4], cs[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-        cs[h] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
-    }
-    const int slot = lane & 7;   // value phase: row slot (8 consecutive lanes = 8 rows)
-    const int grp = lane >> 3;   // value phase: 4-dim group within the block
-
-    // K of a tile is staged before its scores, V only after them, so the
-    // scores of the first tile start as soon as its K has arrived; the next
-    // tile's K and V are in flight in registers meanwhile.
-    // The wave's query slice (G heads x 32 dims) is read by the scores as
-    // wave-uniform chunks of 4 dims x G heads, from one of two places:
-    //  QS = 0: LDS, filled with one vector load per lane issued first, and
-    //          read back as broadcast float4s (for workgroups alone on their
-    //          CU: the scalar loads below would miss a cold scalar cache
-    //          there, several microseconds per call);
-    //  QS = 1: SGPRs, by scalar loads one chunk ahead (once several
-    //          workgroups share a CU: no LDS traffic for the query, which
-    //          would otherwise be about half of the kernel's LDS reads).
-    float4 qv4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!QS && lane < G * 8) qv4 = *(const float4*)(qg + (lane >> 3) * D + 4 * (lane & 7));
-    uint32_t rk[9], rv[VW];
-    load_win(rk, tile_rsrc<D>(SG.k, SG, g, r_begin), voff);
-    load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, r_begin), voffv);
-    // The arguments that were not preloaded, read (and waited for) while the
-    // first tile is in flight.
-    const int32_t n_vis = A.seq[s].seg[seg].n_vis, seq_splits = A.seq[s].n_split, split_off = A.split_off;
-    const float scale_log2e = A.scale_log2e;
-    float* const out = A.out;
-    float* const po = A.po;
-    float* const pm = A.pm;
-    float* const pl = A.pl;
-    float* const part_o = A.part_o;
-    float* const part_m = A.part_m;
-    float* const part_l = A.part_l;
-    asm volatile("" ::"s"(n_vis), "s"(seq_splits), "s"(split_off), "s"(scale_log2e));
-    asm volatile("" ::"s"(out), "s"(po), "s"(pm), "s"(pl), "s"(part_o), "s"(part_m), "s"(part_l));
-    const int r_end = min(r_begin + split_rows, SG.row_lo + n_vis);
-    const int n_tiles = (r_end - r_begin + T - 1) / T;
-    const bool single = seq_splits == 1;
-    const int abs_split = split_off + lsplit;
-    if (!QS && lane < G * 8) *(float4*)&sq[(lane >> 3) * 32 + 4 * (lane & 7)] = qv4;
-    store_win(rk, tk, lane);
-
-    for (int t = 0; t < n_tiles; ++t) {
-        const int row0 = r_begin + t * T;
-        const int nv = min(T, r_end - row0);
-        const bool has_next = t + 1 < n_tiles;
-        if (has_next) load_win(rk, tile_rsrc<D>(SG.k, SG, g, row0 + T), voff);
-        wave_lds_sync();
-
-        // ---- block partial scores, one lane per row
-        float* sxt = sx + (t & 1) * (NB * G * 64);
-        {
-            const uint32_t* rp = tk + lane * 9;
-            uint32_t w[9];
-#pragma unroll
-            for (int j = 0; j < 9; ++j) w[j] = rp[j];
-            // Query chunks of 4 dims x G heads.  From LDS (QS = 0) each is read
-            // just before its FMAs: the empty asm statements keep the reads
-            // from being hoisted, so the query holds one chunk of VGPRs (G = 5:
-            // 125 VGPRs instead of 140 when reading one chunk ahead, so four
-            // workgroups fit a CU instead of three).  From SGPRs (QS = 1) the
-            // scalar loads run one chunk ahead, their order pinned the same way.
-            float dot[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) dot[h] = 0.f;
-            float4 qn[G];
-            if constexpr (QS) {
-                const_f32_ptr qp = (const_f32_ptr)qg;
-                asm volatile("" : "+s"(qp));
-#pragma unroll
-                for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) asm volatile("" : "+v"(dot[h]));
-                float4 qc[G];
-                if constexpr (QS) {
-#pragma unroll
-                    for (int h = 0; h < G; ++h) qc[h] = qn[h];
-                    if (c + 1 < 8) {
-                        const_f32_ptr qp = (const_f32_ptr)qg + 4 * (c + 1);
-                        asm volatile("" : "+s"(qp));
-#pragma unroll
-                        for (int h = 0; h < G; ++h) qn[h] = ldq4(qp + h * D);
-                    }
-                } else {
-                    int off = 4 * c;
-                    asm volatile("" : "+v"(off));
-#pragma unroll
-                    for (int h = 0; h < G; ++h) qc[h] = *(const float4*)&sq[h * 32 + off];
-                }
-                // codes 4c .. 4c+3: bytes 0..3 of dword c+1 of an odd block's
-                // window; bytes 2, 3 of dword c and 0, 1 of dword c+1 of an even
-                // block's (its codes start at byte 2), each converted from its byte
-                const float k0 = ODD ? sbyte(w[c + 1], 0) : sbyte(w[c], 2);
-                const float k1 = ODD ? sbyte(w[c + 1], 1) : sbyte(w[c], 3);
-                const float k2 = ODD ? sbyte(w[c + 1], 2) : sbyte(w[c + 1], 0);
-                const float k3 = ODD ? sbyte(w[c + 1], 3) : sbyte(w[c + 1], 1);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    dot[h] = fmaf(qc[h].x, k0, dot[h]);
-                    dot[h] = fmaf(qc[h].y, k1, dot[h]);
-                    dot[h] = fmaf(qc[h].z, k2, dot[h]);
-                    dot[h] = fmaf(qc[h].w, k3, dot[h]);
-                }
-            }
-            // block scale times the softmax scale (exp2 domain)
-            const float dk = (ODD ? half_hi(w[0]) : half_lo(w[0])) * scale_log2e;
-#pragma unroll
-            for (int h = 0; h < G; ++h) sxt[(wave * G + h) * 64 + lane] = dot[h] * dk;
-        }
-        lds_barrier();
-        store_vwin<VW>(rv, tv, lane);
-        if (has_next) load_vwin<VW>(rv, vtile_rsrc<D, VT>(SG, g, row0 + T), voffv);
-        wave_lds_sync();
-
-        // ---- full scores (same sum order in every wave) and online softmax
-        float sc[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float a = sxt[h * 64 + lane];
-#pragma unroll
-            for (int b = 1; b < NB; ++b) a += sxt[(b * G + h) * 64 + lane];
-            sc[h] = a;
-        }
-        if (nv < T) {
-            // only a split's last tile can be partial
-#pragma unroll
-            for (int h = 0; h < G; ++h) sc[h] = (lane < nv) ? sc[h] : -INFINITY;
-        }
-        {
-            // first tile: start from the score of its first row (always visible)
-            // instead of a wave-wide maximum; the lazy rule below still raises
-            // it if any row passes it by more than kLazyMax
-            if (t == 0) {
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-                    m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[h])));
-            }
-            bool big = false;
-#pragma unroll
-            for (int h = 0; h < G; ++h) big |= sc[h] > m[h] + kLazyMax;
-            if (__builtin_amdgcn_ballot_w64(big)) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float mn = fmaxf(m[h], wave_max(sc[h]));
-                    if (mn > m[h]) {
-                        const float alpha = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
-                        l[h] *= alpha;
-                        if (VT) cs[h] *= alpha;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) o[h][e] *= alpha;
-                        m[h] = mn;
-                    }
-                }
-            }
-        }
-        {
-            // rows past the visible range may hold any bits: their weight is an exact 0
-            const float dv = (lane < nv) ? (ODD ? half_hi(tv[lane * VW]) : half_lo(tv[lane * VW])) : 0.f;
-            float c[GP];
-#pragma unroll
-            for (int h = 0; h < GP; ++h) c[h] = 0.f;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
-                l[h] += p;
-                c[h] = p * dv;
-                if (VT) cs[h] += c[h];
-            }
-#pragma unroll
-            for (int h = 0; h < GP; h += 4) *(float4*)&scw[lane * GP + h] = make_float4(c[h], c[h + 1], c[h + 2], c[h + 3]);
-        }
-        wave_lds_sync();
-
-        // ---- values: 4 dims per lane, 8 rows per pass
-#pragma unroll 4
-        for (int ps = 0; ps < 8; ++ps) {
-            const int r = ps * 8 + slot;
-            uint32_t x = 0;
-            float vq[4];
-            if constexpr (VT == 0) {
-                // dims 4 grp .. 4 grp + 3, bytes picked as for the scores
-                const uint32_t* rp = tv + r * 9;
-                const uint32_t lo = rp[grp], hi = rp[grp + 1];
-                vq[0] = ODD ? sbyte(hi, 0) : sbyte(lo, 2);
-                vq[1] = ODD ? sbyte(hi, 1) : sbyte(lo, 3);
-                vq[2] = ODD ? sbyte(hi, 2) : sbyte(hi, 0);
-                vq[3] = ODD ? sbyte(hi, 3) : sbyte(hi, 1);
-            } else {
-                // dims 4 grp .. 4 grp + 3: low nibbles of code bytes 4 grp .. (grp < 4),
-                // high nibbles of bytes 4 (grp - 4) .. (grp >= 4)
-                const uint32_t* rp = tv + r * 5;
-                const int kq = grp & 3;
-                const uint32_t raw = ODD ? rp[kq + 1] : __builtin_amdgcn_alignbyte(rp[kq + 1], rp[kq], 2);
-                x = (raw >> ((grp >> 2) * 4)) & 0x0F0F0F0Fu;
-            }
-            float c[GP];
-#pragma unroll
-            for (int h = 0; h < GP; h += 4) {
-                const float4 cv = *(const float4*)&scw[r * GP + h];
-                c[h] = cv.x;
-                c[h + 1] = cv.y;
-                c[h + 2] = cv.z;
-                c[h + 3] = cv.w;
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float vv = VT ? (float)((x >> (8 * e)) & 0xFFu) : vq[e];
-#pragma unroll
-                for (int h = 0; h < G; ++h) o[h][e] = fmaf(c[h], vv, o[h][e]);
-            }
-        }
-        wave_lds_sync();
-        if (has_next) store_win(rk, tk, lane);
-    }
-
-    // ---- fold the 8 row slots (same m in every slot; 8 consecutive lanes), finish l
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float x = o[h][e];
-            x += dpp<kDppQuadXor1>(x);
-            x += dpp<kDppQuadXor2>(x);
-            x += dpp<kDppRowHalfMirror>(x);
-            o[h][e] = x;
-        }
-        l[h] = wave_sum(l[h]);
-        if (VT) {
-            const float c8 = 8.f * wave_sum(cs[h]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[h][e] -= c8;
-        }
-    }
-    const int hq0 = g * G;
-    const int dim0 = 32 * wave + 4 * grp;
-    if (slot == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (single && part_o) {
-                *(float4*)&part_o[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
-                    make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-            } else if (single) {
-                const float inv = 1.f / l[h];
-                *(float4*)&out[((size_t)s * n_head_q + hq0 + h) * D + dim0] =
-                    make_float4(o[h][0] * inv, o[h][1] * inv, o[h][2] * inv, o[h][3] * inv);
-            } else {
-                const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-                *(float4*)&po[pi * D + dim0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-            }
-        }
-    }
-    if (wave == 0 && lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if (!single) {
-                const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-                pm[pi] = m[h];
-                pl[pi] = l[h];
-            } else if (part_o) {
-                const size_t sh = (size_t)s * n_head_q + hq0 + h;
-                part_m[sh] = m[h];
-                part_l[sh] = l[h];
-            }
-        }
+    for (int m = 0; m < N; ++m) {
+        const int u = min(64 * m + lane, NU - 1);
+        const int row = u / UR;
+        off[m] = row * stride + 16 * (u - row * UR);
     }
 }
+
+// Offsets of the dwords u = 64 m + lane of a sub-tile (row u / P, dword u % P).
+template <int N, int P, int NU>
+__device__ inline void narrow_offsets(int32_t (&off)[N], int lane, int32_t stride) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const int u = min(64 * m + lane, NU - 1);
+        const int row = u / P;
+        off[m] = row * stride + 4 * (u - row * P);
+    }
+}
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+template <int N, int REG>
+__device__ inline void load_wide(uint32_t (&r)[REG], __amdgpu_buffer_rsrc_t rs, const int32_t (&off)[N]) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off[m], 0, 0);
+        r[4 * m] = x.x;
+        r[4 * m + 1] = x.y;
+        r[4 * m + 2] = x.z;
+        r[4 * m + 3] = x.w;
+    }
+}
+
+template <int N, int REG>
+__device__ inline void load_narrow(uint32_t (&r)[REG], __amdgpu_buffer_rsrc_t rs, const int32_t (&off)[N]) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) r[m] = __builtin_amdgcn_raw_buffer_load_b32(rs, off[m], 0, 0);
+}
+
+template <int N, int REG>
+__device__ inline void store_wide(const uint32_t (&r)[REG], uint32_t* t, int lane) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+        u32x4 x;
+        x.x = r[4 * m];
+        x.y = r[4 * m + 1];
+        x.z = r[4 * m + 2];
+        x.w = r[4 * m + 3];
+        *(u32x4*)&t[4 * (64 * m + lane)] = x;
+    }
+}
+
+template <int N, int REG>
+__device__ inline void store_narrow(const uint32_t (&r)[REG], uint32_t* t, int lane) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) t[64 * m + lane] = r[m];
+}
+
+__device__ inline float xchg16(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+__device__ inline float xchg32(float x, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
+}
+
+// Sum over the 16 lanes of each DPP row, in every lane of the row.
+__device__ inline float row16_sum(float x) {
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppRowHalfMirror>(x);
+    x += dpp<kDppRowMirror>(x);
+    return x;
+}
+
+// Scores of one (row, block): dot[h] += sum over the block's 32 codes of
+// q[h][code] * code, the query of code j broadcast from lane j % 16.
+template <int G, int J>
+struct ScoreCodes {
+    static __device__ __forceinline__ void run(float (&dot)[G], const float (&Q)[G][2], const uint32_t (&cw)[8]) {
+        const float x = (float)(int8_t)(cw[J / 4] >> (8 * (J % 4)));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            if constexpr (J == 0)
+                mul_bc<0>(dot[h], Q[h][0], x);
+            else
+                fmac_bc<J % 16>(dot[h], Q[h][J / 16], x);
+        }
+        ScoreCodes<G, J + 1>::run(dot, Q, cw);
+    }
+};
+template <int G>
+struct ScoreCodes<G, 32> {
+    static __device__ __forceinline__ void run(float (&)[G], const float (&)[G][2], const uint32_t (&)[8]) {}
+};
+
+// Values of one row n of the lane's row set: o[h][e] += c[h] of lane n times
+// the lane's two V values of that row.
+template <int G, int VT, int N>
+struct ValueRows {
+    static __device__ __forceinline__ void run(float (&o)[G][2], const float (&c)[G], const uint8_t* vp,
+                                               int row_bytes) {
+        float x0, x1;
+        // (the empty asm hides the zero extension of the narrow load, so the
+        // bytes are converted by SDWA selects of the loaded register)
+        if constexpr (VT == 0) {
+            uint32_t x = *(const uint16_t*)(vp + N * row_bytes);
+            asm("" : "+v"(x));
+            x0 = (float)(int8_t)x;
+            x1 = (float)(int8_t)(x >> 8);
+        } else {
+            // q4_0: one byte holds dims i (low nibble) and i + 16 (high nibble):
+            // accumulate the low nibble and the whole byte (low + 16 high)
+            uint32_t x = vp[N * row_bytes];
+            asm("" : "+v"(x));
+            x0 = (float)(x & 15u);
+            x1 = (float)(uint8_t)x;
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            fmac_bc<N>(o[h][0], c[h], x0);
+            fmac_bc<N>(o[h][1], c[h], x1);
+        }
+        ValueRows<G, VT, N + 1>::run(o, c, vp, row_bytes);
+    }
+};
+template <int G, int VT>
+struct ValueRows<G, VT, 16> {
+    static __device__ __forceinline__ void run(float (&)[G][2], const float (&)[G], const uint8_t*, int) {}
+};
 
 // The leading arguments (14 dwords: the counts, the query and the first
 // sequence's first segment) are preloaded into SGPRs when the waves start (the
@@ -594,19 +447,18 @@ __device__ __forceinline__ void slice_body(const LaunchArgs& A, const SegDesc& S
 // of a one-sequence launch issues its query and K/V loads without reading its
 // arguments from memory: they sit in memory that the step's K/V stream has
 // evicted from every cache since the layer's previous call.  Everything else
-// comes from the LaunchArgs block, read while the first tile is in flight.
+// comes from the LaunchArgs block, read while the first sub-tile is in flight.
 // kv_seq packs n_head_kv (low 16 bits) and the launch's sequence count.
-template <int D, int G, int VT, int QS>
-__global__ void __launch_bounds__(64 * (D / 32))
-slice_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_rows, const int32_t n_split0,
-             const float* q, const uint8_t* k0, const uint8_t* v0, const int32_t stride0, const int32_t vstride0,
-             const int32_t row_lo0, const int32_t n_rows0, const LaunchArgs A) {
-    using S_ = Slice<D, G>;
-    constexpr int NB = S_::NB, GP = S_::GP, T = S_::T;
-    __shared__ __attribute__((aligned(16))) uint32_t s_kv[NB][2][T * 9];
-    __shared__ __attribute__((aligned(16))) float s_x[2 * NB * G * 64];
-    __shared__ __attribute__((aligned(16))) float s_c[NB][T * GP];
-    __shared__ __attribute__((aligned(16))) float s_q[NB][QS ? 4 : G * 32];
+template <int D, int G, int VT, int WIDE>
+__global__ void __launch_bounds__(256)
+decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_rows, const int32_t n_split0,
+              const float* q, const uint8_t* k0, const uint8_t* v0, const int32_t stride0, const int32_t vstride0,
+              const int32_t row_lo0, const int32_t n_rows0, const LaunchArgs A) {
+    using L_ = Lay<D, VT>;
+    using WL = WaveLds<D, G, VT>;
+    constexpr int NB = L_::NB, R = L_::R, PK = L_::PK, PV = L_::PV, CB = L_::CB, CBV = L_::CBV;
+    constexpr int KW = L_::KW, VW = L_::VW, KN = L_::KN, VN = L_::VN;
+    __shared__ __attribute__((aligned(16))) uint32_t s_lds[4][WL::DWORDS];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -643,13 +495,291 @@ slice_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_ro
         // wait here, so that the one-sequence path meets no pending load
         asm volatile("" ::"s"(SG.k), "s"(SG.v), "s"(SG.stride), "s"(SG.vstride), "s"(SG.row_lo), "s"(SG.n_rows));
     }
-    SG.n_vis = SG.n_split = 0;  // not used: slice_body reads the visible row count itself
-    if (wave & 1)
-        slice_body<D, G, VT, QS, 1>(A, SG, s, seg, g, sp, lsplit, n_head_kv, split_rows, q, wave, lane,
-                                    s_kv[wave][0], s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
-    else
-        slice_body<D, G, VT, QS, 0>(A, SG, s, seg, g, sp, lsplit, n_head_kv, split_rows, q, wave, lane,
-                                    s_kv[wave][0], s_kv[wave][1], s_x, s_c[wave], s_q[wave]);
+    const int r_begin = SG.row_lo + sp * split_rows;
+    const int n_head_q = n_head_kv * G;
+
+    // lane roles
+    const int dr = lane >> 4;           // DPP row
+    const int li = lane & 15;           // lane within it
+    const int b = dr % NB;              // q8_0 block of the head
+    const int rho = 16 * (dr / NB) + li;  // row of the sub-tile (scores, softmax)
+    const int odd = b & 1;              // block starts 2 bytes into a dword
+
+    // Loads.  WIDE: the launch's K/V bases and row strides are 16-byte
+    // multiples, and a sub-tile is read in 16-byte units from the boundary
+    // below each row's head chunk (`lead` bytes before it).  The buffer range
+    // check is per dword: the units of the segment's last readable row that
+    // run past its chunk (always a whole number of dwords) read zeros there
+    // and touch nothing beyond it.  Else the sub-tile is read in dwords from
+    // the chunk start.  Both fill the same LDS layout.  (q8_0 V rows have the
+    // K geometry and share the K offsets.)
+    const int klead = WIDE ? (g * CB) & 15 : 0;
+    const int vlead = WIDE ? (g * CBV) & 15 : 0;
+    constexpr int KO = WIDE ? KW : KN, VO = WIDE ? VW : VN;
+    int32_t koff[KO], voff[VO];
+    if constexpr (WIDE) {
+        wide_offsets<KW, RowUnits<CB>::UR, L_::KUW>(koff, lane, SG.stride);
+        if constexpr (VT) wide_offsets<VW, RowUnits<CBV>::UR, L_::VUW>(voff, lane, SG.vstride);
+    } else {
+        narrow_offsets<KN, PK, R * PK>(koff, lane, SG.stride);
+        if constexpr (VT) narrow_offsets<VN, PV, R * PV>(voff, lane, SG.vstride);
+    }
+    if constexpr (!VT) {
+#pragma unroll
+        for (int m = 0; m < KO; ++m) voff[m] = koff[m];
+    }
+    uint32_t rk[WIDE ? 4 * KW : KN], rv[WIDE ? 4 * VW : VN];
+    // issue the loads of the sub-tile at row r0
+    auto issue = [&](int r0) {
+        const __amdgpu_buffer_rsrc_t kr = sub_rsrc(SG.k, SG.stride, SG.n_rows, CB, g, klead, r0);
+        const __amdgpu_buffer_rsrc_t vr = sub_rsrc(SG.v, SG.vstride, SG.n_rows, CBV, g, vlead, r0);
+        if constexpr (WIDE) {
+            load_wide<KW>(rk, kr, koff);
+            load_wide<VW>(rv, vr, voff);
+        } else {
+            load_narrow<KN>(rk, kr, koff);
+            load_narrow<VN>(rv, vr, voff);
+        }
+    };
+    issue(r_begin + wave * R);
+    float Q[G][2];
+    {
+        const float* qg = q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * b + li;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            Q[h][0] = qg[h * D];
+            Q[h][1] = qg[h * D + 16];
+        }
+    }
+    // The arguments that were not preloaded, read (and waited for) while the
+    // first sub-tile is in flight.
+    const int32_t n_vis = A.seq[s].seg[seg].n_vis, seq_splits = A.seq[s].n_split, split_off = A.split_off;
+    const float scale_log2e = A.scale_log2e;
+    float* const out = A.out;
+    float* const po = A.po;
+    float* const pm = A.pm;
+    float* const pl = A.pl;
+    float* const part_o = A.part_o;
+    float* const part_m = A.part_m;
+    float* const part_l = A.part_l;
+    asm volatile("" ::"s"(n_vis), "s"(seq_splits), "s"(split_off), "s"(scale_log2e));
+    asm volatile("" ::"s"(out), "s"(po), "s"(pm), "s"(pl), "s"(part_o), "s"(part_m), "s"(part_l));
+    const int r_end = min(r_begin + split_rows, SG.row_lo + n_vis);
+    const int n_sub = (r_end - r_begin + R - 1) / R;
+    const bool single = seq_splits == 1;
+    const int abs_split = split_off + lsplit;
+
+    uint32_t* const tk = s_lds[wave];
+    uint32_t* const tv = s_lds[wave] + WL::K;
+    // LDS addresses of this lane's K window (block b of row rho): the scale
+    // dword, and the 9 dwords from which the 32 codes are realigned (an odd
+    // block's codes start one dword later, dword-aligned; an even block's two
+    // bytes into its first dword).  The leads are multiples of 4 bytes.
+    const int kwin = rho * PK + (klead >> 2) + ((34 * b) >> 2);
+    const uint32_t* const kscale_p = tk + kwin;
+    const uint32_t* const kcode_p = tk + kwin + odd;
+    const int kshift = odd ? 0 : 2;
+    const uint32_t* const vscale_p = tv + rho * PV + (vlead >> 2) + ((L_::VB * b) >> 2);
+    // the lane's V values of row 0 of its row set (rows follow PV dwords apart)
+    const uint8_t* const vcode_p = (const uint8_t*)(tv + 16 * (dr / NB) * PV) + vlead + L_::VB * b + 2 +
+                                   (VT ? li : 2 * li);
+
+    float m[G], l[G], o[G][2], cs[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+        cs[h] = 0.f;
+        o[h][0] = o[h][1] = 0.f;
+    }
+    dpp_source_guard(Q);
+
+    for (int t = wave; t < n_sub; t += 4) {
+        const int row0 = r_begin + t * R;
+        const int nv = min(R, r_end - row0);
+        {
+            // Issue priority grows with the sub-tiles this wave has left.  The
+            // SIMD otherwise favours its oldest waves: the first workgroups
+            // placed on a CU ran ahead and finished early (by per-workgroup
+            // timestamps, 64 us against 103 us for the last ones at 131072
+            // rows), leaving the last ones to run at low occupancy.
+            const int rem = (n_sub - t + 3) >> 2;
+            if (rem > 8)
+                __builtin_amdgcn_s_setprio(3);
+            else if (rem > 4)
+                __builtin_amdgcn_s_setprio(2);
+            else if (rem > 2)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
+        if constexpr (WIDE) {
+            store_wide<KW>(rk, tk, lane);
+            store_wide<VW>(rv, tv, lane);
+        } else {
+            store_narrow<KN>(rk, tk, lane);
+            store_narrow<VN>(rv, tv, lane);
+        }
+        if (t + 4 < n_sub) issue(row0 + 4 * R);
+        wave_lds_sync();
+
+        // ---- scores of (row rho, block b), summed over the blocks of the row
+        float sc[G];
+        {
+            uint32_t z[9];
+#pragma unroll
+            for (int j = 0; j < 9; ++j) z[j] = kcode_p[j];
+            const uint32_t kd = *kscale_p;
+            uint32_t cw[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) cw[k] = __builtin_amdgcn_alignbyte(z[k + 1], z[k], kshift);
+            float dot[G];
+            ScoreCodes<G, 0>::run(dot, Q, cw);
+            const float dk = half_lo(kd >> (16 * odd)) * scale_log2e;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                // the product is rounded before the exchange (the empty asm keeps
+                // the compiler from fusing it into the add), so every lane of a
+                // row adds the same two rounded values and holds the same score
+                float x = dot[h] * dk;
+                asm("" : "+v"(x));
+                x += xchg16(x);
+                if constexpr (NB == 4) x += xchg32(x, lane);
+                sc[h] = x;
+            }
+        }
+        if (nv < R) {
+            // only a split's last sub-tile can be partial
+#pragma unroll
+            for (int h = 0; h < G; ++h) sc[h] = (rho < nv) ? sc[h] : -INFINITY;
+        }
+
+        // ---- online softmax (wave-uniform running maximum per head)
+        if (t == wave) {
+            // first sub-tile of the wave: start from the score of its first row
+            // (always visible); the lazy rule below still raises it
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+                m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[h])));
+        }
+        {
+            bool big = false;
+#pragma unroll
+            for (int h = 0; h < G; ++h) big |= sc[h] > m[h] + kLazyMax;
+            if (__builtin_amdgcn_ballot_w64(big)) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mn = fmaxf(m[h], wave_max(sc[h]));
+                    if (mn > m[h]) {
+                        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+                        l[h] *= alpha;
+                        if (VT) cs[h] *= alpha;
+                        o[h][0] *= alpha;
+                        o[h][1] *= alpha;
+                        m[h] = mn;
+                    }
+                }
+            }
+        }
+        float c[G];
+        {
+            // rows past the visible range may hold any bits: their coefficient is an exact 0
+            const uint32_t vd = *vscale_p;
+            const float dv = (rho < nv) ? half_lo(vd >> (16 * odd)) : 0.f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
+                l[h] += p;
+                c[h] = p * dv;
+                if (VT) cs[h] += c[h];
+            }
+        }
+        dpp_source_guard(c);
+
+        // ---- values: the 16 rows of the lane's row set, coefficients broadcast from lane n
+        ValueRows<G, VT, 0>::run(o, c, vcode_p, 4 * PV);
+        wave_lds_sync();
+    }
+
+    // ---- this wave's (m, l, o) to its LDS area, then the four waves merge
+    // l: every lane of a row holds its p, so count block 0's lanes only
+#pragma unroll
+    for (int h = 0; h < G; ++h) l[h] = wave_sum(b == 0 ? l[h] : 0.f);
+    if constexpr (VT) {
+        // sum of the coefficients over the rows of the lane's block
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            cs[h] = row16_sum(cs[h]);
+            if constexpr (NB == 2) cs[h] += xchg32(cs[h], lane);
+        }
+    }
+    if constexpr (NB == 2) {
+        // two row sets: their partial sums meet
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            o[h][0] += xchg32(o[h][0], lane);
+            o[h][1] += xchg32(o[h][1], lane);
+        }
+    }
+    float* const mw = (float*)s_lds[wave];  // m [G], l [G], o [G][D]
+    if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mw[h] = m[h];
+            mw[G + h] = l[h];
+        }
+    }
+    if (dr < NB) {
+        // one row set holds the wave's sums: dims of this lane
+        const int d0 = VT ? 32 * b + li : 32 * b + 2 * li;
+        const int d1 = VT ? d0 + 16 : d0 + 1;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float a0 = o[h][0], a1 = o[h][1];
+            if constexpr (VT) {
+                // low nibbles and whole bytes -> dims i and i + 16, codes offset by 8
+                const float hi = (a1 - a0) * 0.0625f;
+                a0 = a0 - 8.f * cs[h];
+                a1 = hi - 8.f * cs[h];
+            }
+            mw[2 * G + h * D + d0] = a0;
+            mw[2 * G + h * D + d1] = a1;
+        }
+    }
+    __syncthreads();
+    const int hq0 = g * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        const int h = idx / D, d = idx - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, ((const float*)s_lds[w])[h]);
+        float L = 0.f, O = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float* mw2 = (const float*)s_lds[w];
+            const float mk = mw2[h];
+            const float a = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+            L = fmaf(a, mw2[G + h], L);
+            O = fmaf(a, mw2[2 * G + h * D + d], O);
+        }
+        if (single && part_o) {
+            const size_t sh = (size_t)s * n_head_q + hq0 + h;
+            part_o[sh * D + d] = O;
+            if (d == 0) {
+                part_m[sh] = M;
+                part_l[sh] = L;
+            }
+        } else if (single) {
+            out[((size_t)s * n_head_q + hq0 + h) * D + d] = O / L;
+        } else {
+            const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
+            po[pi * D + d] = O;
+            if (d == 0) {
+                pm[pi] = M;
+                pl[pi] = L;
+            }
+        }
+    }
 }
 
 // Merge n partial results (m_k, l_k, o_k) of one (sequence, query head) in
@@ -774,37 +904,30 @@ typedef void (*combine_fn)(int32_t, int32_t, int32_t, const float*, const float*
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
-// The kernel for group G, or null for a scalar query beyond
-// kScalarQueryMaxGroup (the plan never asks for one).
-template <int D, int G, int VT, int QS>
-decode_fn slice_ptr() {
-    if constexpr (QS && G > kScalarQueryMaxGroup) return nullptr;
-    else return slice_kernel<D, G, VT, QS>;
-}
-
-template <int D, int VT, int QS>
-decode_fn pick_slice_g(int G) {
+template <int D, int VT, int WIDE>
+decode_fn pick_decode_g(int G) {
     switch (G) {
-        case 1: return slice_ptr<D, 1, VT, QS>();
-        case 2: return slice_ptr<D, 2, VT, QS>();
-        case 3: return slice_ptr<D, 3, VT, QS>();
-        case 4: return slice_ptr<D, 4, VT, QS>();
-        case 5: return slice_ptr<D, 5, VT, QS>();
-        case 6: return slice_ptr<D, 6, VT, QS>();
-        case 7: return slice_ptr<D, 7, VT, QS>();
-        case 8: return slice_ptr<D, 8, VT, QS>();
+        case 1: return decode_kernel<D, 1, VT, WIDE>;
+        case 2: return decode_kernel<D, 2, VT, WIDE>;
+        case 3: return decode_kernel<D, 3, VT, WIDE>;
+        case 4: return decode_kernel<D, 4, VT, WIDE>;
+        case 5: return decode_kernel<D, 5, VT, WIDE>;
+        case 6: return decode_kernel<D, 6, VT, WIDE>;
+        case 7: return decode_kernel<D, 7, VT, WIDE>;
+        case 8: return decode_kernel<D, 8, VT, WIDE>;
     }
     return nullptr;
 }
 
-template <int QS>
-decode_fn pick_slice_qs(int D, int G, int VT) {
-    if (VT) return D == 128 ? pick_slice_g<128, 1, QS>(G) : pick_slice_g<64, 1, QS>(G);
-    return D == 128 ? pick_slice_g<128, 0, QS>(G) : pick_slice_g<64, 0, QS>(G);
+template <int WIDE>
+decode_fn pick_decode_w(int D, int G, int VT) {
+    if (VT) return D == 128 ? pick_decode_g<128, 1, WIDE>(G) : pick_decode_g<64, 1, WIDE>(G);
+    return D == 128 ? pick_decode_g<128, 0, WIDE>(G) : pick_decode_g<64, 0, WIDE>(G);
 }
 
-decode_fn pick_slice(int D, int G, int VT, bool scalar_query) {
-    return scalar_query ? pick_slice_qs<1>(D, G, VT) : pick_slice_qs<0>(D, G, VT);
+// wide: every K/V base and row stride of the call is a multiple of 16 bytes
+decode_fn pick_decode(int D, int G, int VT, bool wide) {
+    return wide ? pick_decode_w<1>(D, G, VT) : pick_decode_w<0>(D, G, VT);
 }
 
 }  // namespace
@@ -812,11 +935,40 @@ decode_fn pick_slice(int D, int G, int VT, bool scalar_query) {
 
 using namespace kvd;
 
+namespace kvd {
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, asked once per device (the split plan
+// is made for them, so it stays a function of the shapes on a given device).
+// Where no device answers (a host without a GPU planning a workspace size) the
+// plan is made for MI355X's count.
+int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1 || n > 4096) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+}  // namespace
+}  // namespace kvd
+
 extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes) {
     clear_error();
     if (!bytes) return fail(KVD_EINVAL, "bytes is NULL");
     AttendPlan p;
-    const int rc = plan_attend(args, &p);
+    const int rc = plan_attend(args, &p, device_cus());
     if (rc != KVD_OK) return rc;
     *bytes = p.ws_bytes;
     return KVD_OK;
@@ -829,7 +981,7 @@ namespace {
 // write out; else write (o, m, l) at part (layout of merge_kernel's input).
 int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
     AttendPlan p;
-    int rc = plan_attend(a, &p);
+    int rc = plan_attend(a, &p, device_cus());
     if (rc != KVD_OK) return rc;
     if (!part && !a->out) return fail(KVD_EINVAL, "out must not be NULL");
     if (!part && (uintptr_t)a->out % 16) return fail(KVD_EINVAL, "out must be 16-byte aligned");
@@ -840,7 +992,13 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    const decode_fn dk = pick_slice(a->head_dim, p.group, a->v_type, p.scalar_query);
+    bool wide = true;
+    for (size_t i = 0; i < (size_t)a->n_seq * a->n_seg; ++i) {
+        const kvd_kv_seg& g = a->segs[i];
+        const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
+        if (g.n_rows > 0 && (((uintptr_t)g.k | (uintptr_t)g.v) % 16 || g.row_stride % 16 || vs % 16)) wide = false;
+    }
+    const decode_fn dk = pick_decode(a->head_dim, p.group, a->v_type, wide);
     const combine_fn ck = pick_combine(a->head_dim);
     if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 
@@ -899,7 +1057,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         L.scale_log2e = scale_log2e;
         const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);  // the kernel assumes this rounding
         const SegDesc& f = L.seq[0].seg[0];
-        hipLaunchKernelGGL(dk, dim3(grid), dim3(64 * p.waves), 0, (hipStream_t)stream, L.n_items,
+        hipLaunchKernelGGL(dk, dim3(grid), dim3(256), 0, (hipStream_t)stream, L.n_items,
                            L.n_head_kv | (L.n_seq << 16), L.split_rows, f.n_split, L.q, f.k, f.v, f.stride, f.vstride,
                            f.row_lo, f.n_rows, L);
         hipError_t e = hipGetLastError();

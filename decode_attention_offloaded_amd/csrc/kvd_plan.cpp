@@ -34,11 +34,11 @@ int64_t slice_occupancy_cost(int64_t per_cu) {
 // by slice_occupancy_cost.  The cheapest candidate wins, the larger on a tie.
 // On one sequence of 1024 ... 131072 rows x 8 KV heads this picks the
 // measured fastest split or one within 1%.
-int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis) {
+int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis, int64_t n_cus) {
     const int64_t max_k = std::max<int64_t>(1, ceil_div(max_vis, kTileRows));
     int64_t best_k = 1, best_cost = INT64_MAX;
     for (int64_t k = 1; k <= max_k;) {
-        const int64_t per_cu = ceil_div(slice_workgroups(p, n_head_kv, k * kTileRows), kCUs);
+        const int64_t per_cu = ceil_div(slice_workgroups(p, n_head_kv, k * kTileRows), n_cus);
         const int64_t cost = slice_occupancy_cost(per_cu) * per_cu * (k + kSliceOverheadTiles);
         if (cost <= best_cost) {
             best_cost = cost;
@@ -55,8 +55,9 @@ int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vi
 
 }  // namespace
 
-int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
+int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus) {
     if (!a || !p) return fail(KVD_EINVAL, "null argument");
+    if (n_cus < 1 || n_cus > 4096) return fail(KVD_EINVAL, "compute unit count %d out of range", n_cus);
     if (a->n_seq < 1 || a->n_seq > (1 << 20)) return fail(KVD_EINVAL, "n_seq %d out of range", a->n_seq);
     if (a->n_head_kv < 1 || a->n_head_q < 1 || a->n_head_q % a->n_head_kv != 0)
         return fail(KVD_EINVAL, "n_head_q %d must be a positive multiple of n_head_kv %d", a->n_head_q,
@@ -105,6 +106,9 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
                 return fail(KVD_EINVAL, "seq %d seg %d: k and row_stride must be %lld-byte aligned", s, j,
                             (long long)align);
             const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
+            if (a->v_type == KVD_TYPE_Q8_0 && vs != g.row_stride)
+                return fail(KVD_EINVAL, "seq %d seg %d: q8_0 V rows must share the K row stride (%lld != %lld)", s, j,
+                            (long long)vs, (long long)g.row_stride);
             if (g.v_row_stride < 0 || vs < v_row_bytes || vs >= ((int64_t)1 << 25))
                 return fail(KVD_EINVAL, "seq %d seg %d: V row stride %lld (V row bytes %lld, limit 2^25)", s, j,
                             (long long)vs, (long long)v_row_bytes);
@@ -149,11 +153,10 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
     // rows per split: enough splits to fill the chip, at most kMaxSplits per sequence
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
-    // one wave per q8_0 block of the head
-    p->waves = a->head_dim / 32;
+    p->n_cus = n_cus;
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
-        split_rows = (int64_t)kTileRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis);
+        split_rows = (int64_t)kTileRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis, n_cus);
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kTileRows) * kTileRows;
         split_rows = std::max(split_rows, floor_rows);
@@ -162,10 +165,6 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p) {
         if (split_rows > (1 << 24)) split_rows = 1 << 24;
     }
     p->split_rows = (int32_t)split_rows;
-    // Query by scalar loads once several workgroups share a CU (no LDS traffic
-    // for it); from LDS when each CU holds one workgroup, whose scalar loads
-    // would find a cold scalar cache, and for groups too large for the SGPRs.
-    p->scalar_query = G <= kScalarQueryMaxGroup && ceil_div(slice_workgroups(*p, a->n_head_kv, split_rows), kCUs) >= 2;
 
     int64_t base = 0;
     int32_t max_splits = 0;

@@ -13,12 +13,9 @@ namespace kvd {
 constexpr int kTileRows = 64;           // rows per tile of the decode kernel (split sizes are multiples)
 constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
-constexpr int64_t kCUs = 256;              // compute units of the device
+constexpr int kDefaultCUs = 256;          // MI355X compute units, when the device cannot be asked
 constexpr int64_t kSliceOverheadTiles = 3;  // block-sliced fixed work per workgroup, in tiles
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
-// Largest GQA group whose query chunks (this one and the next: 8 G floats)
-// stay in SGPRs without spilling; larger groups read the query from LDS.
-constexpr int kScalarQueryMaxGroup = 5;
 
 struct SegPlan {
     int32_t row_lo;   // first visible row (segment row index)
@@ -38,16 +35,16 @@ struct AttendPlan {
     int32_t group;        // G = n_head_q / n_head_kv
     int32_t chunk_bytes;  // bytes of one head of one row: head_dim / 32 * 34
     int32_t split_rows;
-    int32_t waves;        // waves per decode workgroup (one per q8_0 block of a head)
-    bool scalar_query;    // query chunks by scalar loads (else from LDS)
+    int32_t n_cus;        // compute units the plan was made for
     int32_t max_splits;   // largest per-sequence split count
     int64_t total_splits;
     std::vector<SeqPlan> seq;
     size_t off_pm, off_pl, off_po, ws_bytes;  // workspace: split maxima, sums, outputs
 };
 
-// Validate every argument that does not need the GPU and build the plan.
-// Returns KVD_OK or KVD_EINVAL (with kvd_last_error text).
-int plan_attend(const kvd_attn_args* a, AttendPlan* p);
+// Validate every argument that does not need the GPU and build the plan for a
+// device of n_cus compute units (the plan depends on the shapes and n_cus
+// only).  Returns KVD_OK or KVD_EINVAL (with kvd_last_error text).
+int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus);
 
 }  // namespace kvd

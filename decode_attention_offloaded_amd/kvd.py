@@ -211,13 +211,16 @@ class Workspace:
 
     Calls that share a workspace must be ordered (one stream, or streams
     ordered by events): they write the same partials.  Growing it waits for
-    the device first, so no launch still in flight uses the buffer it drops;
-    under graph capture (where waiting is not allowed) the old buffer is kept
-    instead.
+    the device first, so no launch still in flight uses the buffer it drops.
+    A buffer that a captured graph may use (handed out during capture) is
+    never dropped: when the workspace grows past it, during capture or later,
+    it is kept for the life of the workspace, since the graph can replay into
+    it at any time.
     """
 
     def __init__(self):
         self._buf = {}
+        self._captured = set()  # device indices whose current buffer a captured graph uses
         self._kept = []
 
     def get(self, nbytes: int, device):
@@ -225,16 +228,20 @@ class Workspace:
         if nbytes == 0:
             return None
         key = torch.device(device).index
+        capturing = torch.cuda.is_current_stream_capturing()
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
             if buf is not None:
-                if torch.cuda.is_current_stream_capturing():
+                if capturing or key in self._captured:
                     self._kept.append(buf)
                 else:
                     torch.cuda.synchronize(device)
                 nbytes = max(nbytes, 2 * buf.numel())
             buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             self._buf[key] = buf
+            self._captured.discard(key)
+        if capturing:
+            self._captured.add(key)
         return buf
 
 

@@ -102,9 +102,10 @@ typedef struct kvd_kv_seg {
     int64_t pos0;        /* token position of row 0 */
     int64_t row_stride;  /* bytes between rows; >= row bytes; multiple of 8
                             (head_dim 128) or 4 (head_dim 64); < 2^25 */
-    int64_t v_row_stride;  /* bytes between V rows, or 0 = row_stride; needed when V
-                              rows are q4_0 (shorter); >= V row bytes, multiple of
-                              4, < 2^25 */
+    int64_t v_row_stride;  /* bytes between V rows, or 0 = row_stride.  q8_0 V
+                              rows have the K geometry: 0 or row_stride (else
+                              KVD_EINVAL).  q4_0 V rows are shorter: >= V row
+                              bytes, multiple of 4, < 2^25 */
 } kvd_kv_seg;
 
 /* Value types of the V cache (K is always q8_0).  q4_0: 18-byte blocks, a

@@ -283,6 +283,55 @@ def test_workspace_grows_eagerly_and_under_capture():
         assert torch.equal(out, refs[2]), rep
 
 
+def test_captured_workspace_survives_eager_growth():
+    """A graph captured with a workspace keeps writing its split partials into
+    that buffer on every replay.  Growing the workspace afterwards (an eager
+    call needing more) must not hand that buffer back to the allocator: a
+    tensor allocated next must not share it, and replays must still equal the
+    eager result."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    rng = np.random.default_rng(777)
+
+    def cache(n):
+        kd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
+        vd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
+        return torch.from_numpy(inputs.random_q(rng, 1, 40, 128)).cuda(), [[(kd, vd, 0)]]
+
+    small, big = cache(2048), cache(32768)
+    ref = torch.empty_like(small[0])
+    kvd.attend_decode(small[0], ref, small[1], 8, workspace=kvd.Workspace())
+    torch.cuda.synchronize()
+    ws = kvd.Workspace()
+    s = torch.cuda.Stream()
+    out = torch.full_like(small[0], float("nan"))
+    with torch.cuda.stream(s):
+        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s)   # sizes the workspace
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s)
+    captured = ws._buf[torch.cuda.current_device()]
+    cap_ptr, cap_len = captured.data_ptr(), captured.numel()
+    del captured
+    big_out = torch.empty_like(big[0])
+    kvd.attend_decode(big[0], big_out, big[1], 8, workspace=ws)            # grows the workspace eagerly
+    torch.cuda.synchronize()
+    assert ws._buf[torch.cuda.current_device()].data_ptr() != cap_ptr
+    fillers = [torch.full((cap_len // 4,), 7.0, dtype=torch.float32, device="cuda") for _ in range(4)]
+    for f in fillers:
+        lo, hi = f.data_ptr(), f.data_ptr() + f.numel() * 4
+        assert hi <= cap_ptr or lo >= cap_ptr + cap_len, "a new tensor reuses the captured workspace"
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), rep
+        for f in fillers:
+            assert bool((f == 7.0).all()), rep
+
+
 @pytest.mark.parametrize("v_type", [0, 1])
 def test_more_sequences_than_one_launch(oracle, v_type):
     """37 sequences: the call is split into launches of 16 sequences; outputs,

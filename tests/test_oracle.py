@@ -257,6 +257,61 @@ def test_row_stride_padding_is_ignored(oracle):
     assert np.array_equal(a, b)
 
 
+# ---------------------------------------------------------------- the symmetric entry point
+
+@pytest.mark.parametrize("pad", [0, 24])
+def test_symmetric_entry_one_row_and_gqa(oracle, pad):
+    """kvd_oracle_attend_f64 (q8_0 K and V, one row stride) on its own: a
+    one-row context returns that row's V for every query head of the group, and
+    with every V value of KV head g equal to g + 1 query head h returns
+    floor(h / G) + 1 (also through padded rows)."""
+    hq, hkv, d = 8, 2, 64
+    rng, k, v = _rand_cache(40 + pad, 1, hkv, d)
+    if pad:
+        k = np.concatenate([k, rng.integers(0, 256, (1, pad), dtype=np.uint8)], axis=1)
+        v = np.concatenate([v, rng.integers(0, 256, (1, pad), dtype=np.uint8)], axis=1)
+    q = inputs.random_q(rng, 1, hq, d)
+    out = oracle.attend_symmetric(q, [[(k, v, 0)]], hkv, d)
+    vv = _v_values(oracle, v[:, :inputs.row_bytes(hkv, d)], hkv, d)[0]
+    assert np.array_equal(out[0], vv[np.arange(hq) // (hq // hkv)])
+    n, nb = 6, d // 32
+    _, k, _ = _rand_cache(41 + pad, n, hkv, d)
+    codes = np.zeros((n, hkv * nb, 32), dtype=np.int8)
+    for g in range(hkv):
+        codes[:, g * nb:(g + 1) * nb, :] = g + 1
+    v = inputs.pack_q8_0(codes, np.full((n, hkv * nb), 0x3C00, dtype=np.uint16))
+    if pad:
+        k = np.concatenate([k, rng.integers(0, 256, (n, pad), dtype=np.uint8)], axis=1)
+        v = np.concatenate([v, rng.integers(0, 256, (n, pad), dtype=np.uint8)], axis=1)
+    out = oracle.attend_symmetric(q, [[(k, v, 0)]], hkv, d)
+    np.testing.assert_allclose(out[0], (np.arange(hq) // (hq // hkv) + 1)[:, None] + 0 * out[0], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_seg,window,pad", [(1, 0, 0), (1, 0, 40), (2, 0, 40), (2, 7, 40), (1, 9, 24), (2, 0, 0)])
+def test_symmetric_entry_equals_the_general_entry(oracle, n_seg, window, pad):
+    """kvd_oracle_attend_f64 passes each segment's single row stride to the
+    pinned general entry point as both the K and the V stride: on padded q8_0
+    rows, in one or two segments, with and without a window, the two agree bit
+    for bit (a wrong stride copy in the adapter reads the padding)."""
+    hq, hkv, d, n = 8, 2, 64, 23
+    rng, k, v = _rand_cache(50 + pad + window + n_seg, n, hkv, d)
+    if pad:
+        k = np.concatenate([k, rng.integers(0, 256, (n, pad), dtype=np.uint8)], axis=1)
+        v = np.concatenate([v, rng.integers(0, 256, (n, pad), dtype=np.uint8)], axis=1)
+    q = inputs.random_q(rng, 2, hq, d)
+    if n_seg == 1:
+        segs = [[(k, v, 3)], [(k[:15], v[:15], 0)]]
+    else:
+        segs = [[(k[:9], v[:9], 0), (k[9:], v[9:], 9)], [(k[:4], v[:4], 10), (k[4:15], v[4:15], 14)]]
+    a = oracle.attend_symmetric(q, segs, hkv, d, window=window)
+    b = oracle.attend(q, segs, hkv, d, window=window)
+    assert np.array_equal(a, b)
+    # and the padding really is skipped: the unpadded rows give the same bytes
+    rb = inputs.row_bytes(hkv, d)
+    bare = [[(kk[:, :rb], vv[:, :rb], p0) for (kk, vv, p0) in seq] for seq in segs]
+    assert np.array_equal(a, oracle.attend(q, bare, hkv, d, window=window))
+
+
 # ---------------------------------------------------------------- masks
 
 def test_window_one_returns_newest_v(oracle):
@@ -357,7 +412,7 @@ def test_ring_bytes_reproduce_printed_ring_column(oracle):
         assert abs(b / 1e6 - ring_col) < 1.0, (ctx, b)
         mib = b / 2**20
         assert 0.0 < delta_mib - mib < 3.0, (ctx, delta_mib, mib)
-        # "about three attention layers' K+V": exactly three at depth 1
+        # the page sizes the 128k ring at roughly three layers' K+V: exactly three at depth 1
         assert b == 3 * ctx * 2176
 
 
