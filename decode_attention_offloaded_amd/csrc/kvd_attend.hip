@@ -898,6 +898,18 @@ __global__ void __launch_bounds__(64 * (D / 32)) merge_kernel(const float* parts
     if (lane < 32) out[sh * D + 32 * wave + lane] = O / L;
 }
 
+// Test support for the staging ring: one wave that holds its stream for
+// about `ticks` ticks of the 100 MHz real-time counter, by polling it with
+// sleeps in between; the loop also ends after 2^22 polls whatever the
+// counter says.
+__global__ void __launch_bounds__(64) spin_kernel(uint32_t ticks) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (uint32_t i = 0; i < (1u << 22); ++i) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 >= ticks) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
 typedef void (*decode_fn)(int32_t, int32_t, int32_t, int32_t, const float*, const uint8_t*, const uint8_t*, int32_t,
                           int32_t, int32_t, int32_t, const LaunchArgs);
 typedef void (*combine_fn)(int32_t, int32_t, int32_t, const float*, const float*, const float*, const LaunchArgs);
@@ -962,6 +974,13 @@ int device_cus() {
 }
 
 }  // namespace
+}  // namespace kvd
+
+namespace kvd {
+hipError_t launch_spin(hipStream_t stream, uint32_t us) {
+    hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, stream, us * 100u);
+    return hipGetLastError();
+}
 }  // namespace kvd
 
 extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes) {

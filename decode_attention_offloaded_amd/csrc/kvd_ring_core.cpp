@@ -153,6 +153,15 @@ int Ring::plan(const kvd_stage_args* a) {
     return KVD_OK;
 }
 
+int Ring::transfer_delay(StreamH s) {
+    if (delay_max_us_ == 0) return 0;
+    // xorshift64
+    delay_state_ ^= delay_state_ << 13;
+    delay_state_ ^= delay_state_ >> 7;
+    delay_state_ ^= delay_state_ << 17;
+    return t_->delay(s, (uint32_t)(delay_state_ % ((uint64_t)delay_max_us_ + 1)));
+}
+
 int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
     const int s = (int)(cursor_ % (uint64_t)n_slots_);
     Slot& S = slots_[s];
@@ -182,7 +191,7 @@ int Ring::deliver_prefix(const kvd_stage_args* a, int64_t rows, int* slot_out) {
         if (S.released_once && t_->wait(xfer_[x], S.rel) != 0)
             return fail(KVD_EHIP, "wait(release): %s", t_->error_text());
         for (const Piece& pc : pieces[x])
-            if (pc.n > 0 && t_->copy_h2d(pc.dst, pc.src, pc.n, xfer_[x]) != 0)
+            if (pc.n > 0 && (transfer_delay(xfer_[x]) != 0 || t_->copy_h2d(pc.dst, pc.src, pc.n, xfer_[x]) != 0))
                 return fail(KVD_EHIP, "prefix copy: %s", t_->error_text());
         if (t_->record(S.ready[x], xfer_[x]) != 0) return fail(KVD_EHIP, "record(ready): %s", t_->error_text());
     }
@@ -270,7 +279,8 @@ int Ring::stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out) {
             if (last_xfer_ == S.delivery + 1) {
                 // this layer's prefix is the newest work on the transfer streams:
                 // the tail follows it there and `ready` moves behind the tail
-                if (t_->copy_h2d(dk, hk, kn, xfer_[0]) != 0 || t_->record(S.ready[0], xfer_[0]) != 0 ||
+                if (transfer_delay(xfer_[0]) != 0 || t_->copy_h2d(dk, hk, kn, xfer_[0]) != 0 ||
+                    t_->record(S.ready[0], xfer_[0]) != 0 || transfer_delay(xfer_[1]) != 0 ||
                     t_->copy_h2d(dv, hv, vn, xfer_[1]) != 0 || t_->record(S.ready[1], xfer_[1]) != 0)
                     return fail(KVD_EHIP, "tail copy: %s", t_->error_text());
             } else {
@@ -361,6 +371,14 @@ extern "C" int kvd_ring_tile_rows(int32_t depth, size_t budget_bytes, int64_t ro
     while (rows > 0 && (!ring_need_bytes(depth, rows, row_bytes, row_bytes, &need) || need > budget)) rows -= 64;
     if (rows < 64) return KVD_DECLINED;
     *tile_rows = rows;
+    return KVD_OK;
+}
+
+extern "C" int kvd_ring_set_transfer_delay(kvd_ring* ring, uint32_t max_us, uint64_t seed) {
+    kvd::clear_error();
+    if (!ring) return kvd::fail(KVD_EINVAL, "ring is NULL");
+    if (max_us > 100000) return kvd::fail(KVD_EINVAL, "max_us %u above 100000", max_us);
+    ring->impl.set_transfer_delay(max_us, seed);
     return KVD_OK;
 }
 

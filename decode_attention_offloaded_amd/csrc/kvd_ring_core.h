@@ -42,6 +42,13 @@ public:
     virtual int stream_sync(StreamH s) = 0;
     virtual int event_sync(EventH e) = 0;
     virtual int host_pinned(const void* p, size_t n, int* pinned) = 0;
+    // Test support: hold stream s for about `us` microseconds (bounded), so
+    // that the copies queued after it start late.  No-op by default.
+    virtual int delay(StreamH s, uint32_t us) {
+        (void)s;
+        (void)us;
+        return 0;
+    }
     virtual const char* error_text() = 0;
 };
 
@@ -65,6 +72,12 @@ public:
 
     int stage(const kvd_stage_args* a, StreamH compute, kvd_slot_view* out);
     int release(int32_t layer, StreamH compute);
+    // Test support: before every copy on a transfer stream, a delay of up to
+    // max_us microseconds drawn from a generator seeded with `seed` (0 = off).
+    void set_transfer_delay(uint32_t max_us, uint64_t seed) {
+        delay_max_us_ = max_us;
+        delay_state_ = seed | 1;
+    }
     void stats(kvd_ring_stats* out) const;
     // Wait for outstanding transfers and releases, free every device resource.
     void teardown();
@@ -113,6 +126,9 @@ private:
     uint64_t cursor_ = 0;        // deliveries issued so far
     uint64_t last_xfer_ = 0;     // cursor+1 of the delivery last put on the transfer stream (0 = none)
     kvd_ring_stats st_{};
+    uint32_t delay_max_us_ = 0;
+    uint64_t delay_state_ = 1;
+    int transfer_delay(StreamH s);  // the test-support delay before a transfer-stream copy
 };
 
 }  // namespace kvd

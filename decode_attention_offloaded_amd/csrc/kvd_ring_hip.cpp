@@ -12,6 +12,11 @@
 #include "kvd_ring_core.h"
 
 namespace kvd {
+// One wave that spins for about `us` microseconds (kvd_attend.hip).
+hipError_t launch_spin(hipStream_t stream, uint32_t us);
+}  // namespace kvd
+
+namespace kvd {
 namespace {
 
 class HipTransport final : public Transport {
@@ -59,6 +64,7 @@ public:
         *pinned = 1;
         return 0;
     }
+    int delay(StreamH s, uint32_t us) override { return check(launch_spin((hipStream_t)s, us)); }
     const char* error_text() override { return last_; }
 
 private:

@@ -107,6 +107,8 @@ def _declare(L):
     L.kvd_ring_release.argtypes = [c_void_p, ctypes.c_int32, c_void_p]
     L.kvd_ring_stats_get.restype = c_int
     L.kvd_ring_stats_get.argtypes = [c_void_p, ctypes.POINTER(RingStats), c_size_t]
+    L.kvd_ring_set_transfer_delay.restype = c_int
+    L.kvd_ring_set_transfer_delay.argtypes = [c_void_p, ctypes.c_uint32, ctypes.c_uint64]
     L.kvd_ring_destroy.restype = None
     L.kvd_ring_destroy.argtypes = [c_void_p]
 
@@ -363,6 +365,11 @@ class Ring:
 
     def release(self, layer: int, stream=None):
         _check(lib().kvd_ring_release(self._h, int(layer), ctypes.c_void_p(_stream_handle(stream))))
+
+    def set_transfer_delay(self, max_us: int, seed: int = 1):
+        """Test support: random 0..max_us microsecond holds before every
+        transfer-stream copy (0 = off)."""
+        _check(lib().kvd_ring_set_transfer_delay(self._h, int(max_us), int(seed)))
 
     def stats(self) -> dict:
         st = RingStats()

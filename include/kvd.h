@@ -292,6 +292,16 @@ typedef struct kvd_ring_stats {
 /* Copy the counters into *out (out_size must be >= sizeof(kvd_ring_stats)). */
 int kvd_ring_stats_get(const kvd_ring* ring, kvd_ring_stats* out, size_t out_size);
 
+/* Test support (for callers that check the ring's ordering, not for
+ * production use): from now on, before every copy the ring puts on one of its
+ * transfer streams, that stream is held for a random 0..max_us microseconds
+ * (a one-wave spin kernel polling the real-time counter, bounded), drawn from
+ * a generator seeded with `seed`.  Late deliveries must not change any
+ * output: every consumer waits for its delivery's `ready` events ([R4] What
+ * it does 2: a ready/release event pair per slot).  max_us = 0 turns it off.
+ * Returns KVD_OK, or KVD_EINVAL (NULL ring, max_us above 100000). */
+int kvd_ring_set_transfer_delay(kvd_ring* ring, uint32_t max_us, uint64_t seed);
+
 /* Wait for the transfer streams and every slot's release, then free slots,
  * events and the transfer streams.  NULL is a no-op. */
 void kvd_ring_destroy(kvd_ring* ring);

@@ -154,6 +154,11 @@ def test_ring_create_and_stats_without_device_work():
         r.stage(0, 7, 0x1000, 0x2000, 1088, 10, 9, 10, stream=0)  # bad flags
     with pytest.raises(kvd.KvdError):
         r.stage(0, kvd.STAGE_PREFETCH, 0x1000, 0x2000, 1088, 10, 11, 10, stream=0)  # stable > n_rows
+    # the test-support transfer delay: validated, no device work
+    r.set_transfer_delay(100, 7)
+    r.set_transfer_delay(0)
+    assert L.kvd_ring_set_transfer_delay(r._h, 100001, 1) == kvd.KVD_EINVAL
+    assert L.kvd_ring_set_transfer_delay(None, 10, 1) == kvd.KVD_EINVAL
     r.close()
     L.kvd_ring_destroy(None)
 

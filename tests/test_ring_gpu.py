@@ -25,11 +25,13 @@ def small_cfg():
     return inputs.Config(90, "ring_test", 12, 1, 3000, 40, 8, 128)
 
 
-def run_arm(env, cfg, host, n_rows, depth, budget, tokens, hook=None, after=None):
+def run_arm(env, cfg, host, n_rows, depth, budget, tokens, hook=None, after=None, xfer_delay_us=0, seed=1):
     torch, kvd, stack = env
     st = stack.Stack(torch, kvd, cfg, host, n_rows, depth, budget, new_rows=stack.token_rows(cfg))
     st.on_view = hook
     st.after_attend = after
+    if xfer_delay_us:
+        st.ring.set_transfer_delay(xfer_delay_us, seed)
     outs = []
     for t in range(tokens):
         st.token(t)
@@ -98,6 +100,50 @@ def test_consumer_delays_and_poisoned_slots(env):
             for l in range(cfg.n_layers):
                 assert torch.isfinite(outs[t][l]).all(), (depth, t, l)
                 assert torch.equal(outs[t][l], ref[t][l]), (depth, t, l)
+    host.free()
+
+
+def test_transfer_delays_and_poisoned_slots(env):
+    """Slow deliveries: before every copy on the ring's transfer streams the
+    stream is held for a random 0..5 ms (a spin kernel on that stream, longer
+    than the host takes to enqueue a layer), so prefix and tail copies land
+    after the attention that needs them was enqueued, while every slot is
+    overwritten with 0xFF after its attention and before its release.  An attention that did not wait for its delivery would
+    read the previous layer's bytes or the poison; a delivery that did not wait
+    for the release would be poisoned."""
+    torch, kvd, stack = env
+    cfg = small_cfg()
+    host = stack.HostKV(cfg.n_layers, cfg.n_ctx, cfg.row_bytes)
+    host.fill(inputs, cfg, cfg.n_ctx)
+    ref, _ = run_arm(env, cfg, host, cfg.n_ctx, 0, 0, 2)
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipMemsetAsync.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p]
+
+    def poison(layer, view):
+        if view.pipelined:
+            s = torch.cuda.current_stream().cuda_stream
+            n = host.cap_rows * host.row_bytes
+            assert hip.hipMemsetAsync(view.k, 0xFF, n, s) == 0
+            assert hip.hipMemsetAsync(view.v, 0xFF, n, s) == 0
+
+    import time
+    wall = {}
+    run_arm(env, cfg, host, cfg.n_ctx, 1, 1 << 30, 2)   # warm-up, not timed
+    for depth, seed, delay in ((1, 10, 0), (1, 11, 5000), (2, 12, 5000), (4, 13, 5000)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        outs, s = run_arm(env, cfg, host, cfg.n_ctx, depth, 1 << 30, 2, after=poison, xfer_delay_us=delay, seed=seed)
+        torch.cuda.synchronize()
+        wall[(depth, delay)] = time.perf_counter() - t0
+        assert s["n_acquire_pipelined"] == 2 * cfg.n_layers
+        for t in range(2):
+            for l in range(cfg.n_layers):
+                assert torch.isfinite(outs[t][l]).all(), (depth, t, l)
+                assert torch.equal(outs[t][l], ref[t][l]), (depth, t, l)
+    # the holds are real: at depth 1 each of the 24 deliveries waits 2.5 ms on
+    # average per stream, so the two tokens take tens of milliseconds longer
+    print("wall time of two tokens (s):", wall)
+    assert wall[(1, 5000)] > wall[(1, 0)] + 0.02, wall
     host.free()
 
 
