@@ -32,6 +32,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kvd_internal.h"
 #include "kvd_plan.h"
@@ -1099,6 +1100,64 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
 extern "C" int kvd_attend_decode(const kvd_attn_args* a, void* stream) {
     clear_error();
     return launch_attend(a, stream, nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// kvd_attend_decode_noalloc: the split partials in a file-scope device array
+// instead of a caller's workspace, for callers that cannot allocate.  Every
+// GPU the library runs on holds its own copy of `scratch` until the process
+// ends; all calls on one GPU share it (overlapping calls race).  Nothing in it
+// needs clearing: each split writes its own partials before the combine
+// launch of the same call reads them.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace kvd {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's address of `scratch`, looked up on the device's first
+// call.  Host code uses only this address: the array's own name on the host
+// is a stand-in, not a device address.
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        const hipError_t e = hipGetLastError();
+        return fail(KVD_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVD_EINVAL, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(KVD_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVD_OK;
+}
+}  // namespace
+}  // namespace kvd
+
+extern "C" int kvd_attend_decode_noalloc(const kvd_attn_args* a, void* stream) {
+    clear_error();
+    AttendPlan p;
+    int rc = plan_attend(a, &p, device_cus());
+    if (rc != KVD_OK) return rc;
+    if (p.ws_bytes > kNoAllocScratchBytes)
+        return fail(KVD_EINVAL, "the split partials of this call need %zu bytes; the built-in scratch holds %zu",
+                    p.ws_bytes, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != KVD_OK) return rc;
+    kvd_attn_args b = *a;
+    b.workspace = ws;
+    b.workspace_bytes = kNoAllocScratchBytes;
+    return launch_attend(&b, stream, nullptr);
 }
 
 extern "C" int kvd_attend_decode_partial(const kvd_attn_args* a, float* partial, void* stream) {

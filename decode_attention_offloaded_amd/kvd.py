@@ -88,6 +88,8 @@ def _declare(L):
     L.kvd_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(c_size_t)]
     L.kvd_attend_decode.restype = c_int
     L.kvd_attend_decode.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
+    L.kvd_attend_decode_noalloc.restype = c_int
+    L.kvd_attend_decode_noalloc.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
     L.kvd_attend_decode_partial.restype = c_int
     L.kvd_attend_decode_partial.argtypes = [ctypes.POINTER(AttnArgs), c_void_p, c_void_p]
     L.kvd_attend_merge.restype = c_int
@@ -268,6 +270,21 @@ def attend_decode(q, out, segs, n_head_kv: int, window: int = 0, scale: Optional
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel()
     _check(lib().kvd_attend_decode(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
+    return out
+
+
+def attend_decode_noalloc(q, out, segs, n_head_kv: int, window: int = 0, scale: Optional[float] = None,
+                          q_pos=None, split_rows: int = 0, stream=None, v_type: int = TYPE_Q8_0):
+    """kvd_attend_decode_noalloc: as attend_decode, with the split partials in
+    the library's built-in device array (no workspace, no allocation).  Calls
+    on one GPU share that array and must be ordered."""
+    import torch
+    if not (q.is_cuda and out.is_cuda) or q.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("q and out must be float32 CUDA tensors")
+    if not (q.is_contiguous() and out.is_contiguous()):
+        raise ValueError("q and out must be contiguous")
+    a, keep = make_args(q, out, segs, n_head_kv, window, scale, q_pos, split_rows, v_type)
+    _check(lib().kvd_attend_decode_noalloc(ctypes.byref(a), ctypes.c_void_p(_stream_handle(stream))))
     return out
 
 

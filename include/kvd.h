@@ -152,6 +152,18 @@ int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
  * visible row, workspace too small) or KVD_EHIP (launch failure). */
 int kvd_attend_decode(const kvd_attn_args* args, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): as
+ * kvd_attend_decode, but the split partials live in a fixed device array
+ * built into the library (8 MiB per GPU, held until the process ends), so
+ * the call allocates nothing; args->workspace and args->workspace_bytes are
+ * ignored.  A call whose partials need more than 8 MiB (see
+ * kvd_attend_workspace_bytes) returns KVD_EINVAL and enqueues nothing.
+ * Every call on one GPU uses the same array: calls that may overlap in time
+ * on one GPU (different streams, not ordered by events) race; order them.
+ * Returns KVD_OK, KVD_EINVAL or KVD_EHIP. */
+int kvd_attend_decode_noalloc(const kvd_attn_args* args, void* stream);
+
 /* Tile-streamed attention ("F5 — Advanced KV Cache Techniques", F5-opt W4,
  * M7 Rolling KV: a slot pool, a tile loop and an inter-tile online-softmax
  * merge of the per-tile results).  A layer's rows are attended in tiles, one
