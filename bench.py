@@ -13,8 +13,13 @@ Default run (one JSON line on stdout):
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the same workload.
   * pipeline: per-token time of the host-resident 64-layer stack at 16384
-    rows, ordered (depth 0) vs pipelined (depth 1, 128 MiB ring), with the
-    measured pinned host-to-device link peak.
+    rows, ordered (depth 0) vs pipelined (depth 1, 128 MiB ring), against the
+    pinned host-to-device plateau probed the way the ring copies (two streams).
+  * device_memory_table / long_context: the page's Device-memory table on this
+    machine (4096 ... 65536 rows, ring size, device-memory growth, declines)
+    and the 131072-row depth x budget sweep.
+  * batched, tiled, residency, asymmetric, head_split: the other host-resident
+    workloads.
 """
 from __future__ import annotations
 
@@ -48,6 +53,10 @@ def algorithmic_bytes(n_rows, n_head_kv, head_dim, n_head_q, n_seq=1):
 
 def device_resident(args, torch, kvd, inputs):
     c = inputs.config(1)
+    if args.rows != c.n_ctx:
+        # another context length of the same geometry (profiling runs)
+        import dataclasses
+        c = dataclasses.replace(c, n_ctx=args.rows)
     L = args.layers
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(c.seed)
@@ -199,34 +208,37 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
 
 # ---------------------------------------------------------------- host link + pipeline
 
-def link_peak(torch):
-    """Pinned host -> device copy bandwidth (GB/s): one copy on one stream at
-    1 MiB ... 1 GiB, and two equal copies on two streams at once (the ring's
-    configuration: K and V on their own DMA engines); median of 10 timed runs
-    (5 at 1 GiB) after one untimed.  The peak is the best plateau."""
-    dev = torch.device("cuda:0")
+def link_peak(kvd):
+    """Pinned host-to-device copy rate as the ring copies (kvd_link_probe:
+    hipHostMalloc'ed source, hipMemcpyAsync on non-blocking streams, HIP-event
+    timed, median of 10 runs, 5 at 1 GiB): one stream, and the bytes split
+    over two streams (the ring's two transfer streams, one DMA engine each),
+    at 16 MiB ... 1 GiB.  Returns (figures, one-stream plateau, two-stream
+    plateau)."""
     res = {}
-    s0, s1 = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+    for mib in (16, 64, 256, 1024):
+        for ns in (1, 2):
+            res["%dx%dMiB" % (ns, mib)] = round(kvd.link_probe(mib << 20, ns, 10 if mib <= 256 else 5), 2)
+    one = max(v for k, v in res.items() if k.startswith("1x"))
+    two = max(v for k, v in res.items() if k.startswith("2x"))
+    return res, one, two
 
-    def run(n, streams):
-        hs = [torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in streams]
-        ds = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in streams]
-        times = []
-        for _ in range(11 if n <= (256 << 20) else 6):
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for s, h, d in zip(streams, hs, ds):
-                with torch.cuda.stream(s):
-                    d.copy_(h, non_blocking=True)
-            torch.cuda.synchronize()
-            times.append(time.perf_counter() - t0)
-        t = float(np.median(times[1:]))
-        return round(n * len(streams) / t / 1e9, 2)
 
-    for mib in (1, 16, 64, 256, 1024):
-        res["1x%dMiB" % mib] = run(mib << 20, [s0])
-    for mib in (16, 64, 256):
-        res["2x%dMiB" % mib] = run(mib << 20, [s0, s1])
+def frac_link(res, link):
+    """Staged GB/s of every arm over the two-stream plateau (the ring's
+    configuration); ordered arms copy on one stream, so they are also given
+    against the one-stream plateau."""
+    figures, one, two = link
+    res["link_GBps_by_size"] = figures
+    res["link_plateau_1stream_GBps"] = one
+    res["link_plateau_2stream_GBps"] = two
+    for arm in res["arms"].values():
+        gbs = arm.get("staged_GBps")
+        if gbs is None:
+            continue
+        arm["frac_link"] = round(gbs / two, 4)
+        if arm.get("depth") == 0:
+            arm["frac_link_1stream"] = round(gbs / one, 4)
     return res
 
 
@@ -270,17 +282,12 @@ def pipeline(args, torch, kvd, inputs, link):
     """Host-resident 64-layer stack at 16384 rows: ordered (depth 0) vs pipelined
     (depth 1, 128 MiB ring), against the pinned H2D link peak measured here."""
     from decode_attention_offloaded_amd import stack
-    peak = max(link.values())
-    log("pinned H2D link: %s GB/s" % link)
+    log("pinned H2D link (GB/s): %s" % (link[0],))
     c = inputs.config(2)
     res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1, "1x"),
                                   budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log)
-    res["link_GBps_by_MiB"] = link
-    res["link_peak_GBps"] = peak
     res["link_environment"] = link_environment(torch)
-    for arm in res["arms"].values():
-        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
-    return res
+    return frac_link(res, link)
 
 
 def batched(args, torch, kvd, inputs, link):
@@ -293,10 +300,7 @@ def batched(args, torch, kvd, inputs, link):
     res = bt.run_batched(torch, kvd, inputs, c, n_layers=args.batched_layers, depths=(0, 1),
                          budget_bytes=1 << 30, tokens=args.batched_tokens, warmup=2, log=log,
                          distinct_layers=4)
-    peak = max(link.values())
-    res["link_peak_GBps"] = peak
-    for arm in res["arms"].values():
-        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    frac_link(res, link)
     log("batched: %s" % {k: (v["ms_per_token"], v["staged_GBps"]) for k, v in res["arms"].items()})
     return res
 
@@ -310,10 +314,7 @@ def tiled(args, torch, kvd, inputs, link):
     res = tl.run_tiled(torch, kvd, inputs, c, n_layers=args.tiled_layers, depths=(0, 1), budget_bytes=128 << 20,
                        tokens=args.tiled_tokens, warmup=2, log=log, distinct_layers=4)
     res.pop("outs", None)
-    peak = max(link.values())
-    res["link_peak_GBps"] = peak
-    for arm in res["arms"].values():
-        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    frac_link(res, link)
     log("tiled (%d rows per tile, %d tiles per layer): %s" % (res["tile_rows"], res["tiles_per_layer"], {
         k: (v["ms_per_token"], v["staged_GBps"]) for k, v in res["arms"].items()}))
     return res
@@ -354,7 +355,7 @@ def residency(args, torch, kvd, inputs, link):
     c = inputs.config(3)
     L, n = args.residency_layers, c.n_ctx
     lb = 2 * n * c.row_bytes
-    peak = max(link.values())
+    peak = link[2]
     cms = layer_compute_ms(torch, kvd, inputs, n)
     arms, plans = [], {}
     for gib in (1, 4):
@@ -369,7 +370,7 @@ def residency(args, torch, kvd, inputs, link):
     res = stack.run_residency(torch, kvd, inputs, c, arms, n_layers=L, tokens=args.residency_tokens, warmup=2,
                               log=log, distinct_layers=4)
     res["compute_ms_per_layer"] = round(cms, 4)
-    res["link_peak_GBps"] = peak
+    res["link_plateau_2stream_GBps"] = peak
     res["plans"] = plans
     for gib, plan in plans.items():
         pick = "%sGiB_%s+%d" % (gib, "ring" if plan["use_ring"] else "ordered", plan["n_resident"])
@@ -388,10 +389,7 @@ def asymmetric(args, torch, kvd, inputs, link):
     c = inputs.config(2)
     res = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1),
                                   budget_bytes=128 << 20, tokens=args.pipe_tokens, warmup=3, log=log, v_type=1)
-    peak = max(link.values())
-    res["link_peak_GBps"] = peak
-    for arm in res["arms"].values():
-        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    frac_link(res, link)
     # device-resident 4096 rows, 64 distinct layers per graph, a query per layer
     c1 = inputs.config(1)
     dev = torch.device("cuda:0")
@@ -445,34 +443,104 @@ def head_split(args, torch, kvd, inputs, link):
     from decode_attention_offloaded_amd import headsplit, stack
     c = inputs.config(3)
     L = args.residency_layers
-    peak = max(link.values())
     hs = headsplit.run_headsplit(torch, kvd, inputs, c, 3, n_layers=L, depths=(0, 1), budget_bytes=1 << 30,
                                  tokens=args.residency_tokens, warmup=2, log=log, distinct_layers=4)
     k_layers = L * 3 // 8
     ls = stack.run_residency(torch, kvd, inputs, c, [("ring+%d" % k_layers, 1, 1 << 30, k_layers),
                                                      ("ordered+%d" % k_layers, 0, 0, k_layers)],
                              n_layers=L, tokens=args.residency_tokens, warmup=2, log=log, distinct_layers=4)
-    for arm in hs["arms"].values():
-        arm["frac_link"] = round(arm["staged_GBps"] / peak, 4)
+    frac_link(hs, link)
     log("head split 3/8: %s; layer split %d/%d: %s" % (
         {k: v["ms_per_token"] for k, v in hs["arms"].items()}, k_layers, L,
         {k: v["ms_per_token"] for k, v in ls["arms"].items()}))
-    return {"head_split": hs, "layer_split": ls, "link_peak_GBps": peak}
+    return {"head_split": hs, "layer_split": ls}
 
 
-def long_context(args, torch, kvd, inputs):
-    """131072 rows x 64 layers host-resident: depth 0/1/2 x budget 128 MiB / 1 GiB."""
+def golden_ring_table():
+    """The [R4] Device-memory table as kept in tests/golden/ring_table.txt:
+    {context: (peak-VRAM delta MiB, ring column)}."""
+    rows = {}
+    with open(os.path.join(ROOT, "tests", "golden", "ring_table.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                ctx, delta, ring = (int(x) for x in line.split())
+                rows[ctx] = (delta, ring)
+    return rows
+
+
+def device_memory_table(args, torch, kvd, inputs, link):
+    """The shape of the [R4] Device-memory table on this machine: a 64-layer
+    host-resident stack (40/8 heads, head_dim 128, bf16 GEMV stand-in) at
+    4096 ... 65536 rows, ordered (depth 0) against pipelined (depth 1) per
+    token, with the ring's size and the device-memory growth of each arm.  A
+    128 MiB budget declines from 32768 rows on; there a larger budget (512 MiB
+    at 32768, 1 GiB at 65536) engages the ring.  The ring column and the
+    declines are checked against the page's table (tests/golden/ring_table.txt)."""
+    from decode_attention_offloaded_amd import stack
+    c = inputs.config(2)
+    golden = golden_ring_table()
+    plan = [(4096, ("0", "1@128")), (16384, ("0", "1@128")), (32768, ("0", "1@128", "1@512")),
+            (65536, ("0", "1@128", "1@1024"))]
+    out = {"layers": args.devmem_layers, "rows": {}, "checks": {}}
+    for n, arms in plan:
+        tokens = max(3, min(args.devmem_tokens, args.devmem_tokens * 16384 // n))
+        r = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.devmem_layers, depths=arms,
+                                    budget_bytes=128 << 20, tokens=tokens, warmup=2, log=log, n_rows=n,
+                                    distinct_layers=4)
+        frac_link(r, link)
+        out["rows"][str(n)] = r
+        out["checks"][str(n)] = ring_checks(n, r, golden, c.row_bytes)
+        log("device memory %d rows: %s" % (n, {k: (v["ms_per_token"], v["declined"], v["ring_engaged_bytes"],
+                                                    v["vram_delta_bytes"]) for k, v in r["arms"].items()}))
+    return out
+
+
+def ring_checks(n, res, golden, row_bytes, slack=16 << 20):
+    """Against the ordered arm of the same run (the page's delta column is
+    pipelined minus ordered peak memory): an engaged ring is (depth + 2) slots
+    x n rows x (K + V) bytes, within its budget, grows device memory by its
+    size (within `slack`: the caching allocator's own pools move by a few MiB
+    between arms), and at depth 1 matches the page's ring column (decimal MB)
+    within 1; a ring over its budget declines and grows nothing."""
+    need1 = 3 * n * 2 * row_bytes
+    base = res["arms"]["0"]["vram_delta_bytes"]
+    ok, notes = True, []
+    for name, arm in res["arms"].items():
+        if arm["depth"] == 0:
+            continue
+        budget = arm["budget_bytes"]
+        need = (arm["depth"] + 2) * n * 2 * row_bytes
+        grow = arm["vram_delta_bytes"] - base
+        if need > budget:
+            good = arm["declined"] == 1 and arm["ring_engaged_bytes"] == 0 and abs(grow) <= slack
+        else:
+            good = (arm["declined"] == 0 and arm["ring_engaged_bytes"] == need and abs(grow - need) <= slack)
+        if arm["depth"] == 1 and n in golden and arm["ring_engaged_bytes"]:
+            good = good and abs(need1 / 1e6 - golden[n][1]) < 1.0
+        arm["vram_growth_over_ordered_bytes"] = int(grow)
+        ok = ok and good
+        notes.append("%s: need %d B, budget %d B, %s, device memory over the ordered arm %+d B" % (
+            name, need, budget, "declined" if arm["declined"] else "engaged %d B" % arm["ring_engaged_bytes"], grow))
+    if n in golden:
+        notes.append("page: ring column %d (MB), VRAM delta %d MiB; 3 x n x 2176 B = %.2f MB" % (
+            golden[n][1], golden[n][0], need1 / 1e6))
+    return {"ok": bool(ok), "notes": notes}
+
+
+def long_context(args, torch, kvd, inputs, link):
+    """131072 rows x 64 layers host-resident, whole-layer ring: depth 0/1/2 x
+    budget 128 MiB / 1 GiB (depth 1 needs 816 MiB: only 1 GiB engages it;
+    depth 2 needs 1088 MiB: neither does)."""
     from decode_attention_offloaded_amd import stack
     c = inputs.config(3)
-    out = {}
-    for budget_mib in (128, 1024):
-        r = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers, depths=(0, 1, 2),
-                                    budget_bytes=budget_mib << 20, tokens=args.long_tokens, warmup=2, log=log,
-                                    distinct_layers=4)
-        out[str(budget_mib)] = r
-        log("long context, budget %d MiB: %s" % (budget_mib, {k: (v["ms_per_token"], v["declined"])
-                                                              for k, v in r["arms"].items()}))
-    return out
+    r = stack.run_host_resident(torch, kvd, inputs, c, n_layers=args.pipe_layers,
+                                depths=("0", "1@128", "2@128", "1@1024", "2@1024"), budget_bytes=128 << 20,
+                                tokens=args.long_tokens, warmup=2, log=log, distinct_layers=4)
+    frac_link(r, link)
+    r["checks"] = ring_checks(c.n_ctx, r, golden_ring_table(), c.row_bytes)
+    log("long context: %s" % {k: (v["ms_per_token"], v["declined"]) for k, v in r["arms"].items()})
+    return r
 
 
 def hbm_stream_ceiling(torch, gib=4, reps=7):
@@ -551,37 +619,98 @@ def calibration_copy(torch, mib=256):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(target_s=15.0):
-    import oracle
-    from decode_attention_offloaded_amd import inputs
-    c = inputs.config(1)
-    cores = len(os.sched_getaffinity(0))
-    r = c.layer_rng(0)
-    k = inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)
-    v = inputs.random_kv_rows(r, c.n_ctx, c.n_head_kv, c.head_dim)
-    q = inputs.random_q(r, 1, c.n_head_q, c.head_dim)
-    t0 = time.perf_counter()
-    oracle.attend(q, [[(k, v, 0)]], c.n_head_kv, c.head_dim, threads=cores)
-    one = time.perf_counter() - t0
-    reps = max(1, int(target_s / max(one, 1e-3)))
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.attend(q, [[(k, v, 0)]], c.n_head_kv, c.head_dim, threads=cores)
-    dt = time.perf_counter() - t0
-    b = algorithmic_bytes(c.n_ctx, c.n_head_kv, c.head_dim, c.n_head_q)
-    cpu = "unknown"
+def cpu_model():
+    """The CPU as /proc/cpuinfo names it, with the count of sockets and of
+    logical CPUs it lists."""
+    names, physical, logical, ident = [], set(), 0, {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k == "model name":
+                    names.append(v.strip())
+                    logical += 1
+                elif k == "physical id":
+                    physical.add(v.strip())
+                elif k in ("vendor_id", "cpu family", "model", "stepping", "cache size", "cpu MHz") and k not in ident:
+                    ident[k] = v.strip()
     except OSError:
         pass
-    return {"value": round(b * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": "%d calls of the 4096-row, 40/8-head, head_dim-128 layer (fp64 oracle, OpenMP over "
-                      "query heads), %.1f s; %s" % (reps, dt, cpu),
-            "ms_per_layer": round(dt / reps * 1e3, 2)}
+    model = names[0] if names else "unknown"
+    return {"model_name": model, "sockets": len(physical) or None, "logical_cpus_listed": logical or None,
+            "vendor": ident.get("vendor_id"), "family": ident.get("cpu family"), "model": ident.get("model"),
+            "stepping": ident.get("stepping"), "cache": ident.get("cache size"), "mhz": ident.get("cpu MHz")}
+
+
+def cpu_baseline(target_s=6.0):
+    """The fp64 oracle on this host's cores, after the GPU legs (never beside
+    them), as the plan has it: single-threaded and on every core of the
+    process's affinity set, on one layer of each workload -- the 4096-row
+    layer, a 16384-row layer, a 131072-row layer, and one full-attention and
+    one 4096-row-window layer of the 16-sequence batch.  Median of up to 5
+    timed calls after one untimed (fewer for calls over ~1 s, so the whole
+    leg stays within about a minute; a call over 2 s is timed once, with no
+    untimed call before it).  `value` is the 4096-row layer on every core, in
+    the bench's unit."""
+    import oracle
+    from decode_attention_offloaded_amd import inputs
+    from decode_attention_offloaded_amd.batched import cfg4_lengths
+    cores = len(os.sched_getaffinity(0))
+    runs = {}
+
+    def timed(name, q, segs, hkv, d, threads, window, nbytes):
+        t0 = time.perf_counter()
+        oracle.attend(q, segs, hkv, d, threads=threads, window=window)
+        one = time.perf_counter() - t0
+        # a call over 2 s is its own measurement (no separate untimed call)
+        n = 5 if one < 0.5 else 3 if one < 2.0 else 0
+        ts = [one] if n == 0 else []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            oracle.attend(q, segs, hkv, d, threads=threads, window=window)
+            ts.append(time.perf_counter() - t0)
+        dt = float(np.median(ts))
+        runs[name] = {"ms_per_layer": round(dt * 1e3, 2), "GBps": round(nbytes / dt / 1e9, 4), "threads": threads,
+                      "timed_calls": len(ts), "untimed_first_call": n > 0, "bytes_per_layer": nbytes}
+
+    work = []
+    for cfg, n in ((1, 4096), (2, 16384), (3, 131072)):
+        c = inputs.config(cfg)
+        r = c.layer_rng(0)
+        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        q = inputs.random_q(r, 1, c.n_head_q, c.head_dim)
+        work.append(("%d rows" % n, q, [[(k, v, 0)]], c, 0, algorithmic_bytes(n, c.n_head_kv, c.head_dim, c.n_head_q)))
+    c = inputs.config(4)
+    r = c.layer_rng(0)
+    lens = [int(x) for x in cfg4_lengths(c)]
+    segs, nb_full, nb_win = [], 0, 0
+    for n in lens:
+        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
+        h = n // 2
+        segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
+        nb_full += 2 * n * c.row_bytes
+        nb_win += 2 * min(n, 4096) * c.row_bytes
+    q4 = inputs.random_q(r, len(lens), c.n_head_q, c.head_dim)
+    qb = 2 * len(lens) * c.n_head_q * c.head_dim * 4
+    work.append(("16 sequences, full attention", q4, segs, c, 0, nb_full + qb))
+    work.append(("16 sequences, 4096-row window", q4, segs, c, 4096, nb_win + qb))
+    t_all = time.perf_counter()
+    for threads in (1, cores):
+        for name, q, sg, c, window, nbytes in work:
+            timed("%s, %d thread%s" % (name, threads, "s" if threads > 1 else ""), q, sg, c.n_head_kv, c.head_dim,
+                  threads, window, nbytes)
+    head = runs["4096 rows, %d thread%s" % (cores, "s" if cores > 1 else "")]
+    cpu = cpu_model()
+    return {"value": head["GBps"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "one 4096-row, 40/8-head, head_dim-128 layer per call (fp64 oracle, OpenMP over query heads) "
+                      "on %d threads, median of %d calls; the plan's other workloads and the single-thread runs are "
+                      "under 'runs' (%.0f s in all); CPU: %s (family %s model %s)" % (
+                          cores, head["timed_calls"], time.perf_counter() - t_all, cpu["model_name"], cpu["family"],
+                          cpu["model"]),
+            "ms_per_layer": head["ms_per_layer"], "cpu": cpu, "runs": runs}
 
 
 # sources that decide the decode kernels' HBM traffic: the kernels and the split plan
@@ -601,56 +730,6 @@ def traffic_source_sha():
         text = re.sub(r"//[^\n]*", " ", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()
-
-
-def cpu_baseline_extra(target_s=10.0):
-    """The oracle on more of the workloads (opt-in, --cpu-extra): the 4096-row
-    layer on one core; one layer at 16384 and at 131072 rows and the
-    16-sequence batch (full and 4096-row window) on every core."""
-    import oracle
-    from decode_attention_offloaded_amd import inputs
-    from decode_attention_offloaded_amd.batched import cfg4_lengths
-    cores = len(os.sched_getaffinity(0))
-    res = {}
-
-    def timed(name, q, segs, hkv, d, threads, window, b):
-        t0 = time.perf_counter()
-        oracle.attend(q, segs, hkv, d, threads=threads, window=window)
-        one = time.perf_counter() - t0
-        reps = max(1, int(target_s / max(one, 1e-3)))
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            oracle.attend(q, segs, hkv, d, threads=threads, window=window)
-        dt = (time.perf_counter() - t0) / reps
-        res[name] = {"ms_per_layer": round(dt * 1e3, 2), "GBps": round(b / dt / 1e9, 4), "threads": threads,
-                     "calls": reps}
-
-    for cfg, n, threads in ((1, 4096, 1), (2, 16384, cores), (3, 131072, cores)):
-        c = inputs.config(cfg)
-        r = c.layer_rng(0)
-        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
-        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
-        q = inputs.random_q(r, 1, c.n_head_q, c.head_dim)
-        timed("%d rows, %d thread%s" % (n, threads, "s" if threads > 1 else ""), q, [[(k, v, 0)]], c.n_head_kv,
-              c.head_dim, threads, 0, algorithmic_bytes(n, c.n_head_kv, c.head_dim, c.n_head_q))
-    c = inputs.config(4)
-    r = c.layer_rng(0)
-    lens = [int(x) for x in cfg4_lengths(c)]
-    segs, nb_full, nb_win = [], 0, 0
-    for n in lens:
-        k = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
-        v = inputs.random_kv_rows(r, n, c.n_head_kv, c.head_dim)
-        h = n // 2
-        segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
-        nb_full += 2 * n * c.row_bytes
-        nb_win += 2 * min(n, 4096) * c.row_bytes
-    q = inputs.random_q(r, len(lens), c.n_head_q, c.head_dim)
-    qb = 2 * len(lens) * c.n_head_q * c.head_dim * 4
-    timed("16 sequences, full attention, %d threads" % cores, q, segs, c.n_head_kv, c.head_dim, cores, 0,
-          nb_full + qb)
-    timed("16 sequences, 4096-row window, %d threads" % cores, q, segs, c.n_head_kv, c.head_dim, cores, 4096,
-          nb_win + qb)
-    return {"cores": cores, "kind": "oracle", "workloads": res}
 
 
 def measured_traffic():
@@ -677,6 +756,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--rows", type=int, default=4096,
+                    help="context of the device-resident leg (4096 = the headline workload; others for profiling)")
+    ap.add_argument("--ceiling", type=int, default=1, help="measure the streaming ceiling")
     ap.add_argument("--curve", type=int, default=1)
     ap.add_argument("--pipeline", type=int, default=1)
     ap.add_argument("--pipe-layers", type=int, default=64)
@@ -693,10 +775,11 @@ def main():
     ap.add_argument("--residency-tokens", type=int, default=5)
     ap.add_argument("--asym", type=int, default=1, help="run the q8_0 K / q4_0 V legs")
     ap.add_argument("--headsplit", type=int, default=1, help="run the per-head residency split leg")
-    ap.add_argument("--long", type=int, default=0, help="also run the 131072-row depth/budget sweep")
-    ap.add_argument("--long-tokens", type=int, default=5)
-    ap.add_argument("--cpu-extra", type=int, default=0,
-                    help="also time the oracle single-threaded and on the 16384/131072-row and batched layers")
+    ap.add_argument("--long", type=int, default=1, help="run the 131072-row depth/budget sweep")
+    ap.add_argument("--long-tokens", type=int, default=3)
+    ap.add_argument("--devmem", type=int, default=1, help="run the device-memory table (4096 ... 65536 rows)")
+    ap.add_argument("--devmem-layers", type=int, default=64)
+    ap.add_argument("--devmem-tokens", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -722,19 +805,20 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "decode attention, device-resident q8_0 KV: 1 sequence x 4096 rows, 40 query / "
-                               "8 KV heads, head_dim 128; one step = 64 distinct layer caches",
-                   "n_ctx": 4096, "n_head_q": 40, "n_head_kv": 8, "head_dim": 128,
+        "config": {"workload": "decode attention, device-resident q8_0 KV: 1 sequence x %d rows, 40 query / "
+                               "8 KV heads, head_dim 128; one step = %d distinct layer caches" % (
+                                   args.rows, d["layers_per_step"]),
+                   "n_ctx": args.rows, "n_head_q": 40, "n_head_kv": 8, "head_dim": 128,
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel<128,5,0,1> + combine_kernel<128> (one call)",
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
-        "hbm_stream_ceiling": hbm_stream_ceiling(torch),
+        "hbm_stream_ceiling": hbm_stream_ceiling(torch) if args.ceiling else None,
         "calibration_copy_bytes": calib,
     }
-    if args.curve:
+    if args.curve and args.ceiling:
         # what one streaming launch moving a call's algorithmic bytes reaches
         c1 = inputs.config(1)
         same = {}
@@ -742,8 +826,8 @@ def main():
             same[str(n)] = stream_same_bytes(torch, algorithmic_bytes(n, c1.n_head_kv, c1.head_dim, c1.n_head_q))
         out["hbm_stream_ceiling"]["same_bytes_as_call"] = same
     log("streaming ceiling: %s" % out["hbm_stream_ceiling"])
-    link = (link_peak(torch) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
-                                 or args.headsplit) else None)
+    link = (link_peak(kvd) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
+                               or args.headsplit or args.long or args.devmem) else None)
     if args.pipeline:
         out["pipeline"] = pipeline(args, torch, kvd, inputs, link)
     if args.batched:
@@ -756,12 +840,13 @@ def main():
         out["asymmetric"] = asymmetric(args, torch, kvd, inputs, link)
     if args.headsplit:
         out["head_split"] = head_split(args, torch, kvd, inputs, link)
+    if args.devmem:
+        out["device_memory_table"] = device_memory_table(args, torch, kvd, inputs, link)
     if args.long:
-        out["long_context"] = long_context(args, torch, kvd, inputs)
+        out["long_context"] = long_context(args, torch, kvd, inputs, link)
     if args.cpu_baseline:
+        # after every GPU leg, so the oracle never competes with DMA for host memory
         out["cpu_baseline"] = cpu_baseline()
-    if args.cpu_extra:
-        out["cpu_baseline_extra"] = cpu_baseline_extra()
     print(json.dumps(out), flush=True)
 
 

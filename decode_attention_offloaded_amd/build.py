@@ -26,7 +26,8 @@ NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # them from memory where the firmware does not preload.
 KERNARG_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 HIP_SOURCES = ["kvd_attend.hip"]
-HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp"]
+HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp",
+                "kvd_probe.cpp"]
 
 
 def _compile(src: str) -> str:

@@ -252,6 +252,9 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
         weights = [(torch.randn(m, n, dtype=torch.bfloat16, device=dev, generator=gen) * 0.02)
                    for _ in range(n_layers)]
     rows_fn = token_rows(cfg, v_type=v_type)
+    # an arm is a depth, "<depth>x" for that depth with cross-step look-ahead,
+    # or "<depth>@<MiB>" for that depth under its own budget
+    arm_budget = {d: (int(str(d).split("@")[1]) << 20 if "@" in str(d) else budget_bytes) for d in depths}
     order = list(depths) + list(reversed(depths))
     # One compute stream for every arm, as an engine has one: streams share the
     # process's few hardware queues, and a fresh stream per arm would make the
@@ -263,9 +266,8 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         free0 = torch.cuda.mem_get_info(dev)[0]
-        # an arm is a depth, or "<depth>x" for that depth with cross-step look-ahead
-        depth, cross = int(str(d).rstrip("x")), cross_step or str(d).endswith("x")
-        st = Stack(torch, kvd, cfg, host, n_rows, depth, budget_bytes, gemv_weights=weights, new_rows=rows_fn,
+        depth, cross = int(str(d).split("@")[0].rstrip("x")), cross_step or str(d).endswith("x")
+        st = Stack(torch, kvd, cfg, host, n_rows, depth, arm_budget[d], gemv_weights=weights, new_rows=rows_fn,
                    stream=compute, cross_step=cross)
         for t in range(warmup):
             st.token(t)
@@ -285,7 +287,8 @@ def run_host_resident(torch, kvd, inputs, cfg, n_layers=64, depths=(0, 1), budge
     for d in depths:
         ms = float(np.median(times[d]))
         s = stats[d]
-        res["arms"][str(d)] = {"depth": int(str(d).rstrip("x")), "cross_step": cross_step or str(d).endswith("x"),
+        res["arms"][str(d)] = {"depth": int(str(d).split("@")[0].rstrip("x")),
+                               "cross_step": cross_step or str(d).endswith("x"), "budget_bytes": arm_budget[d],
                                "ms_per_token": round(ms, 3), "tokens_per_s": round(1e3 / ms, 3),
                                "staged_GBps": round(bytes_token / (ms * 1e-3) / 1e9, 2),
                                "ring_engaged_bytes": s["ring_bytes"] if s["engaged"] else 0,

@@ -71,6 +71,17 @@ const char* kvd_last_error(void);
 /* Library version string, e.g. "kvd 0.1.0 gfx950". */
 const char* kvd_version(void);
 
+/* Host-link probe (measurement support): the pinned host-to-device copy rate
+ * the staging ring can expect.  Copies `bytes` from hipHostMalloc'ed memory to
+ * a hipMalloc'ed buffer with hipMemcpyAsync, split evenly over n_streams
+ * non-blocking streams (the ring uses two, one DMA engine each), `reps` timed
+ * times after one untimed; *gbps = bytes / median time, in GB/s (10^9 B/s).
+ * Allocates and frees its own buffers and streams (synchronous).  ("F5 —
+ * Advanced KV Cache Techniques", W1: probe the pinned host-to-device plateau.)
+ * Returns KVD_OK, KVD_EINVAL (bytes outside [4096, 8 GiB], n_streams outside
+ * [1, 4], reps outside [1, 1000], NULL gbps) or KVD_EHIP. */
+int kvd_link_probe(size_t bytes, int32_t n_streams, int32_t reps, double* gbps);
+
 /* ==================================================================== attention
  * kvd_attend_decode: single-token decode attention over q8_0 K/V.
  *

@@ -222,3 +222,11 @@ def test_v_type_and_v_stride_are_validated():
     a4, _ = _args(segs=segs4, v_type=kvd.TYPE_Q4_0)
     a8, _ = _args()
     assert kvd.workspace_bytes(a4) == kvd.workspace_bytes(a8)
+
+
+def test_link_probe_validates_before_touching_the_gpu():
+    L = kvd.lib()
+    g = ctypes.c_double(0.0)
+    for args in ((100, 2, 10), (1 << 20, 0, 10), (1 << 20, 5, 10), (1 << 20, 2, 0), ((9 << 30), 1, 1)):
+        assert L.kvd_link_probe(args[0], args[1], args[2], ctypes.byref(g)) == kvd.KVD_EINVAL, args
+    assert L.kvd_link_probe(1 << 20, 2, 10, None) == kvd.KVD_EINVAL
