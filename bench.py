@@ -93,6 +93,8 @@ def device_resident(args, torch, kvd, inputs):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
     ms_step = ms / args.steps
+    plan_args, _keep = kvd.make_args(qs[0], outs[0], [[(ks[0], vs[0], 0)]], c.n_head_kv)
+    split_rows, waves, n_splits = kvd.attend_plan(plan_args)
     launches = args.steps * L
     us_launch = ms * 1e3 / launches
     per_launch = algorithmic_bytes(c.n_ctx, c.n_head_kv, c.head_dim, c.n_head_q)
@@ -113,6 +115,7 @@ def device_resident(args, torch, kvd, inputs):
     return {
         "ms_per_step": ms_step, "value": gbs, "us_per_launch": us_launch, "bytes_per_launch": per_launch,
         "layers_per_step": L, "curve": curve,
+        "plan": {"split_rows": split_rows, "waves": waves, "splits": n_splits},
         "ws": ws, "q": qs[0], "k": ks[0], "v": vs[0],
     }
 
@@ -812,7 +815,8 @@ def main():
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "decode_kernel<128,5,0,1> + combine_kernel<128> (one call)",
+                     "kernel": "decode_kernel<128,5,0,1,%d> + combine_kernel<128> (one call; %d splits of %d "
+                               "rows)" % (d["plan"]["waves"], d["plan"]["splits"], d["plan"]["split_rows"]),
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
         "device_curve": d["curve"],
         "hbm_stream_ceiling": hbm_stream_ceiling(torch) if args.ceiling else None,

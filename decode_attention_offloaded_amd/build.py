@@ -25,6 +25,10 @@ NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # 14 user SGPRs left for them); the code object keeps a prologue that loads
 # them from memory where the firmware does not preload.
 KERNARG_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
+# MFMA accumulators in ordinary VGPRs (the register file is unified): with the
+# accumulator registers, the softmax rescale of the output accumulators made
+# the compiler copy all of them out and back on every loop iteration.
+MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 HIP_SOURCES = ["kvd_attend.hip"]
 HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp",
                 "kvd_probe.cpp"]
@@ -34,7 +38,7 @@ def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON
     if src.endswith(".hip"):
-        cmd += ["--offload-arch=" + ARCH] + CODE_OBJECT + NO_PACKED_FP32 + KERNARG_PRELOAD
+        cmd += ["--offload-arch=" + ARCH] + CODE_OBJECT + NO_PACKED_FP32 + KERNARG_PRELOAD + MFMA_VGPR
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -10,13 +10,12 @@
 // merged by their running maxima and sums).
 //
 // Shape of the work.  A split = one (sequence, KV head, row range) = one
-// workgroup of four waves.  Each wave walks its own sub-tiles of the split's
-// rows (every fourth one) over all head_dim dims of the head and keeps its own
-// online-softmax state; the four states meet in LDS once, at the end of the
-// split.  Inside a wave, lane 16 r + i works on q8_0 block r % (D / 32) of one
-// row; the query and the softmax weights reach the lanes that need them through
-// DPP row broadcasts folded into the multiply-adds (details at decode_kernel).
-// The arguments a split needs before its first loads are kernel arguments that
+// workgroup of W = 4, 8 or 12 waves (the plan picks W from the work per CU).
+// Each wave walks its own 16-row sub-tiles of the split (every W-th one) over
+// all head_dim dims of the head and keeps its own online-softmax state; the W
+// states meet in LDS once, at the end of the split.  The two contractions of a
+// sub-tile run on the matrix cores (decode_kernel has the details).  The
+// arguments a split needs before its first loads are kernel arguments that
 // the hardware preloads into SGPRs; the rest are read while the first sub-tile
 // is in flight.
 // A split with siblings writes an unnormalised partial (m, l, o) to the
@@ -25,7 +24,6 @@
 // split plan.  (Merging inside the first launch would need device-scope
 // release/acquire between workgroups, which on this chip writes back and
 // invalidates the whole L2 of an XCD per workgroup.)
-// No MFMA: one query row per head is not a dense contraction.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -147,106 +145,10 @@ __device__ inline void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ inline float half_lo(uint32_t w) {
-    _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-    return (float)h;
-}
-
-// ---------------------------------------------------------------------------
-// The decode kernel.  A workgroup (four waves) takes one split: one
-// (sequence, KV head, row range).  The waves walk the split's rows in
-// sub-tiles of R rows, wave w taking sub-tiles w, w + 4, w + 8, ..., and each
-// keeps its own online-softmax state; the four states are merged through LDS
-// once, at the end of the split.  There is no barrier inside the row loop.
-//
-// Lanes.  A wave's 64 lanes are four DPP rows of 16.  Lane 16 dr + i works on
-// q8_0 block b = dr % NB of the head (dims 32 b .. 32 b + 31) and on row
-// 16 (dr / NB) + i of the sub-tile, so R = 16 * 4 / NB rows (16 at head_dim
-// 128, 32 at 64).
-//   * Scores: a lane converts the 32 codes of its (row, block) and multiplies
-//     them with the query; the query value for code j of block b sits in lane
-//     j % 16 of the DPP row (register j / 16) and reaches every lane of the row
-//     through a DPP row broadcast folded into the FMA (v_fmac_f32_dpp
-//     row_newbcast), so a lane holds 2 G query floats instead of 32 G.  The
-//     block partials of a row meet through two lane exchanges (ds_swizzle and
-//     ds_bpermute, no LDS memory) in the same order in every lane.
-//   * Softmax: every lane of a row holds the row's scores; the running maximum
-//     of each head is wave-uniform and is raised only when a score passes it
-//     by more than kLazyMax (log2 units), so most sub-tiles need no wave-wide
-//     maximum and no rescale.  A lane's weight p times its block's V scale is
-//     the coefficient c of that (row, block).
-//   * Values: the 16 lanes of a DPP row take two dims each of the row's block
-//     (q8_0: dims 2i, 2i + 1; q4_0: dims i, i + 16), and loop over the 16 rows
-//     of their row set; the coefficient of row n comes from lane n of the same
-//     DPP row by the same broadcast, so a lane keeps 2 G accumulators.
-// Loads: a sub-tile of one KV head is R rows x 34 NB bytes (2176 bytes of K at
-// either head size), read as 9 dword loads per lane over consecutive units of
-// the sub-tile (one or two rows per instruction) and copied to a wave-private
-// LDS tile in the same order; the next sub-tile is in flight in registers
-// while this one is computed.
+// The running maximum of each (wave, query head) is raised only when a score
+// passes it by more than kLazyMax (log2 units), so most sub-tiles need no
+// exchange of maxima and no rescale; the weights exp2(s - m) stay below 2^8.
 constexpr float kLazyMax = 8.0f;
-
-// v_fmac_f32 with its first source taken from lane N of the lane's DPP row
-// (row_newbcast, gfx90a and later).  Written as inline assembly because the
-// compiler does not fold a DPP move into a multiply-add; the source must not
-// be written by a VALU instruction in the two instructions before (the callers
-// separate such writes with kvd::dpp_source_guard).
-template <int N>
-__device__ __forceinline__ void fmac_bc(float& acc, float src, float x);
-#define KVD_FMAC_BC(N)                                                                                       \
-    template <>                                                                                              \
-    __device__ __forceinline__ void fmac_bc<N>(float& acc, float src, float x) {                            \
-        asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"                       \
-            : "+v"(acc)                                                                                      \
-            : "v"(src), "v"(x));                                                                             \
-    }
-KVD_FMAC_BC(0)
-KVD_FMAC_BC(1)
-KVD_FMAC_BC(2)
-KVD_FMAC_BC(3)
-KVD_FMAC_BC(4)
-KVD_FMAC_BC(5)
-KVD_FMAC_BC(6)
-KVD_FMAC_BC(7)
-KVD_FMAC_BC(8)
-KVD_FMAC_BC(9)
-KVD_FMAC_BC(10)
-KVD_FMAC_BC(11)
-KVD_FMAC_BC(12)
-KVD_FMAC_BC(13)
-KVD_FMAC_BC(14)
-KVD_FMAC_BC(15)
-#undef KVD_FMAC_BC
-
-// acc = (src of lane N of the DPP row) * x, the first term of a sum.
-template <int N>
-__device__ __forceinline__ void mul_bc(float& acc, float src, float x);
-#define KVD_MUL_BC(N)                                                                                        \
-    template <>                                                                                              \
-    __device__ __forceinline__ void mul_bc<N>(float& acc, float src, float x) {                             \
-        asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:" #N " row_mask:0xf bank_mask:0xf"                        \
-            : "=v"(acc)                                                                                      \
-            : "v"(src), "v"(x));                                                                             \
-    }
-KVD_MUL_BC(0)
-#undef KVD_MUL_BC
-
-// Two wait states after the last VALU write of the registers that the
-// following DPP broadcasts read; the registers pass through the statement so
-// the compiler keeps every such write before it.
-template <int N>
-__device__ __forceinline__ void dpp_source_guard(float (&r)[N]) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k]));
-    asm volatile("s_nop 1" ::: "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void dpp_source_guard(float (&r)[N][2]) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) asm volatile("" : "+v"(r[k][0]), "+v"(r[k][1]));
-    asm volatile("s_nop 1" ::: "memory");
-}
 
 constexpr int gcd16(int x) { return (x & 15) == 0 ? 16 : (x & 7) == 0 ? 8 : (x & 3) == 0 ? 4 : (x & 1) == 0 ? 2 : 1; }
 
@@ -377,70 +279,121 @@ __device__ inline float xchg32(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __builtin_bit_cast(int, x)));
 }
 
-// Sum over the 16 lanes of each DPP row, in every lane of the row.
-__device__ inline float row16_sum(float x) {
-    x += dpp<kDppQuadXor1>(x);
-    x += dpp<kDppQuadXor2>(x);
-    x += dpp<kDppRowHalfMirror>(x);
-    x += dpp<kDppRowMirror>(x);
-    return x;
+// ---------------------------------------------------------------------------
+// The decode kernel.  For one KV head, the G query heads of its group against
+// 16 rows are a (16 x D) by (D x G) product for the scores and a (D x 16) by
+// (16 x G) product for the values, both dense; they run on MFMA with G padded
+// to 16 ("F5 -- Advanced KV Cache Techniques", M3 What shipped: the query
+// heads of a GQA group share every K/V row they read).  On the vector units
+// alone (no packed fp32 here) the int8 conversions and fp32 multiply-adds of
+// a sub-tile took longer than its transfer from HBM.
+//
+// Lanes: n = lane % 16, gq = lane / 16.  A 16x16 MFMA result leaves element
+// (4 gq + j, n) in register j of lane (gq, n); its first operand takes row n
+// from lane (gq, n) and its second operand column n, both over the k-slots of
+// lane group gq (the same slots in both, so which k sits in which slot is
+// this code's choice).
+//   * Scores, per q8_0 block b: S_b[row][head] = sum over the block's 32 dims
+//     of code[row][dim] * q'[head][dim], a 16x16x32 f16 product per query part:
+//     lane (gq, n) gives the codes of row n at dims 32 b + 8 gq .. + 7
+//     (binary16 holds every int8 code exactly) and q' of head n at the same
+//     dims.  The query is fp32 and enters as two binary16 parts, hi = f16(q')
+//     and lo = f16(q' - hi); their products with the codes are exact and add
+//     up in fp32, so the score keeps about 22 significant bits of the query.
+//     q' = q * scale * log2(e) * 2^(15 - E), E per head such that the largest
+//     |q'| lies in [2^14, 2^15): neither part overflows or runs out of range.
+//     Lane (gq, n) then holds rows 4 gq + j of head n and applies their block
+//     scales: S = 2^(E - 15) sum_b dk_b S_b, in log2 units.
+//   * Softmax: lane (gq, n) keeps the running maximum, the sum and the output
+//     of head n.  The four lane groups of a head exchange their maxima
+//     (ds_swizzle, ds_bpermute) only when a score passes the maximum by more
+//     than kLazyMax.
+//   * Values, per block b and half c: O[dim][head] += sum over the 16 rows of
+//     code[row][dim] * (p[row][head] * dv[row][b]), a 16x16x16 bf16 product
+//     whose second operand has the score layout (rows 4 gq + j of head n in
+//     lane (gq, n)), so the weights never move between lanes.  They enter as
+//     two bfloat16 parts (about 17 significant bits; bfloat16 has the fp32
+//     exponent range, which binary16 lacks for a weight times an arbitrary
+//     binary16 scale).  q8_0: MFMA row i of half c is dim 32 b + 2 i + c (a lane
+//     reads one 2-byte pair per row and block); q4_0: dims 32 b + i and
+//     32 b + 16 + i (the two nibbles of byte i), accumulated as the low nibble
+//     and the whole byte (low + 16 high), the offset of 8 taken off through
+//     the sum of the weights.
+// Loads: a sub-tile of one KV head (16 or 32 rows x 34 D / 32 bytes) is read
+// in 16-byte units over consecutive rows (or in dwords where a base or row
+// stride is not a multiple of 16 bytes), one unit per lane per instruction,
+// and copied to a wave-private LDS tile in the same order; the next sub-tile
+// is in flight in registers while this one is computed.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Byte N of w as a signed integer, converted to binary16 (exact) by an SDWA
+// byte select: into the low half of a new register (high half zero), or into
+// the high half of d (low half kept).
+template <int N>
+__device__ __forceinline__ uint32_t i8_f16_lo(uint32_t w);
+template <int N>
+__device__ __forceinline__ void i8_f16_hi(uint32_t& d, uint32_t w);
+#define KVD_I8_F16_LO(N)                                                                                    \
+    template <>                                                                                              \
+    __device__ __forceinline__ uint32_t i8_f16_lo<N>(uint32_t w) {                                           \
+        uint32_t d;                                                                                          \
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_" #N         \
+            : "=v"(d)                                                                                        \
+            : "v"(w));                                                                                       \
+        return d;                                                                                            \
+    }
+#define KVD_I8_F16_HI(N)                                                                                    \
+    template <>                                                                                              \
+    __device__ __forceinline__ void i8_f16_hi<N>(uint32_t & d, uint32_t w) {                                 \
+        asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_" #N    \
+            : "+v"(d)                                                                                        \
+            : "v"(w));                                                                                       \
+    }
+// (a pair starts on an even byte: low halves take bytes 0 and 2, high halves 1 and 3)
+KVD_I8_F16_LO(0)
+KVD_I8_F16_LO(2)
+KVD_I8_F16_HI(1)
+KVD_I8_F16_HI(3)
+#undef KVD_I8_F16_LO
+#undef KVD_I8_F16_HI
+
+// Codes 2 P and 2 P + 1 of the 8 that start S bytes into z[0], as a binary16 pair.
+template <int S, int P>
+__device__ __forceinline__ uint32_t code_pair_f16(const uint32_t (&z)[3]) {
+    constexpr int i0 = S + 2 * P, i1 = i0 + 1;
+    uint32_t d = i8_f16_lo<i0 % 4>(z[i0 / 4]);
+    i8_f16_hi<i1 % 4>(d, z[i1 / 4]);
+    return d;
 }
 
-// Scores of one (row, block): dot[h] += sum over the block's 32 codes of
-// q[h][code] * code, the query of code j broadcast from lane j % 16.
-template <int G, int J>
-struct ScoreCodes {
-    static __device__ __forceinline__ void run(float (&dot)[G], const float (&Q)[G][2], const uint32_t (&cw)[8]) {
-        const float x = (float)(int8_t)(cw[J / 4] >> (8 * (J % 4)));
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            if constexpr (J == 0)
-                mul_bc<0>(dot[h], Q[h][0], x);
-            else
-                fmac_bc<J % 16>(dot[h], Q[h][J / 16], x);
-        }
-        ScoreCodes<G, J + 1>::run(dot, Q, cw);
-    }
-};
-template <int G>
-struct ScoreCodes<G, 32> {
-    static __device__ __forceinline__ void run(float (&)[G], const float (&)[G][2], const uint32_t (&)[8]) {}
-};
+// The 8 K codes of a lane (S bytes into the LDS dword at zp) as the f16
+// operand of a 16x16x32 product.
+template <int S>
+__device__ __forceinline__ half8_t kcodes_f16(const uint32_t* zp) {
+    uint32_t z[3];
+    z[0] = zp[0];
+    z[1] = zp[1];
+    z[2] = S ? zp[2] : 0u;
+    const u32x4 h = {code_pair_f16<S, 0>(z), code_pair_f16<S, 1>(z), code_pair_f16<S, 2>(z),
+                     code_pair_f16<S, 3>(z)};
+    return __builtin_bit_cast(half8_t, h);
+}
 
-// Values of one row n of the lane's row set: o[h][e] += c[h] of lane n times
-// the lane's two V values of that row.
-template <int G, int VT, int N>
-struct ValueRows {
-    static __device__ __forceinline__ void run(float (&o)[G][2], const float (&c)[G], const uint8_t* vp,
-                                               int row_bytes) {
-        float x0, x1;
-        // (the empty asm hides the zero extension of the narrow load, so the
-        // bytes are converted by SDWA selects of the loaded register)
-        if constexpr (VT == 0) {
-            uint32_t x = *(const uint16_t*)(vp + N * row_bytes);
-            asm("" : "+v"(x));
-            x0 = (float)(int8_t)x;
-            x1 = (float)(int8_t)(x >> 8);
-        } else {
-            // q4_0: one byte holds dims i (low nibble) and i + 16 (high nibble):
-            // accumulate the low nibble and the whole byte (low + 16 high)
-            uint32_t x = vp[N * row_bytes];
-            asm("" : "+v"(x));
-            x0 = (float)(x & 15u);
-            x1 = (float)(uint8_t)x;
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            fmac_bc<N>(o[h][0], c[h], x0);
-            fmac_bc<N>(o[h][1], c[h], x1);
-        }
-        ValueRows<G, VT, N + 1>::run(o, c, vp, row_bytes);
-    }
-};
-template <int G, int VT>
-struct ValueRows<G, VT, 16> {
-    static __device__ __forceinline__ void run(float (&)[G][2], const float (&)[G], const uint8_t*, int) {}
-};
+// Two floats as a bfloat16 pair (round to nearest even), x0 in the low half.
+__device__ __forceinline__ uint32_t bf16_pair(float x0, float x1) {
+    const float2_t v = {x0, x1};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// binary16 in the low (HI = 0) or high half of w, to fp32.
+template <int HI>
+__device__ __forceinline__ float f16_half(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(HI ? (w >> 16) : (w & 0xffffu)));
+}
 
 // The leading arguments (14 dwords: the counts, the query and the first
 // sequence's first segment) are preloaded into SGPRs when the waves start (the
@@ -450,16 +403,18 @@ struct ValueRows<G, VT, 16> {
 // evicted from every cache since the layer's previous call.  Everything else
 // comes from the LaunchArgs block, read while the first sub-tile is in flight.
 // kv_seq packs n_head_kv (low 16 bits) and the launch's sequence count.
-template <int D, int G, int VT, int WIDE>
-__global__ void __launch_bounds__(256)
+template <int D, int G, int VT, int WIDE, int W>
+__global__ void __launch_bounds__(64 * W)
 decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_rows, const int32_t n_split0,
-              const float* q, const uint8_t* k0, const uint8_t* v0, const int32_t stride0, const int32_t vstride0,
-              const int32_t row_lo0, const int32_t n_rows0, const LaunchArgs A) {
+                   const float* q, const uint8_t* k0, const uint8_t* v0, const int32_t stride0,
+                   const int32_t vstride0, const int32_t row_lo0, const int32_t n_rows0, const LaunchArgs A) {
     using L_ = Lay<D, VT>;
     using WL = WaveLds<D, G, VT>;
-    constexpr int NB = L_::NB, R = L_::R, PK = L_::PK, PV = L_::PV, CB = L_::CB, CBV = L_::CBV;
+    constexpr int NB = L_::NB, R = L_::R, PK = L_::PK, PV = L_::PV, CB = L_::CB, CBV = L_::CBV, VB = L_::VB;
     constexpr int KW = L_::KW, VW = L_::VW, KN = L_::KN, VN = L_::VN;
-    __shared__ __attribute__((aligned(16))) uint32_t s_lds[4][WL::DWORDS];
+    constexpr int RS = R / 16;  // 16-row groups of a sub-tile
+    static_assert(G <= 16, "one MFMA column per query head of the group");
+    __shared__ __attribute__((aligned(16))) uint32_t s_lds[W][WL::DWORDS];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -493,27 +448,22 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         SG.vstride = d.vstride;
         SG.row_lo = d.row_lo;
         SG.n_rows = d.n_rows;
-        // wait here, so that the one-sequence path meets no pending load
         asm volatile("" ::"s"(SG.k), "s"(SG.v), "s"(SG.stride), "s"(SG.vstride), "s"(SG.row_lo), "s"(SG.n_rows));
     }
     const int r_begin = SG.row_lo + sp * split_rows;
     const int n_head_q = n_head_kv * G;
 
-    // lane roles
-    const int dr = lane >> 4;           // DPP row
-    const int li = lane & 15;           // lane within it
-    const int b = dr % NB;              // q8_0 block of the head
-    const int rho = 16 * (dr / NB) + li;  // row of the sub-tile (scores, softmax)
-    const int odd = b & 1;              // block starts 2 bytes into a dword
+    const int n = lane & 15;   // MFMA row / column of the lane
+    const int gq = lane >> 4;  // lane group: k-slots, and rows 4 gq .. 4 gq + 3 of a result
 
     // Loads.  WIDE: the launch's K/V bases and row strides are 16-byte
     // multiples, and a sub-tile is read in 16-byte units from the boundary
-    // below each row's head chunk (`lead` bytes before it).  The buffer range
-    // check is per dword: the units of the segment's last readable row that
-    // run past its chunk (always a whole number of dwords) read zeros there
-    // and touch nothing beyond it.  Else the sub-tile is read in dwords from
-    // the chunk start.  Both fill the same LDS layout.  (q8_0 V rows have the
-    // K geometry and share the K offsets.)
+    // below each row's head chunk (`lead` bytes before it, a multiple of 4).
+    // The buffer range check is per dword: the units of the segment's last
+    // readable row that run past its chunk (always a whole number of dwords)
+    // read zeros there and touch nothing beyond it.  Else the sub-tile is read
+    // in dwords from the chunk start.  Both fill the same LDS layout.  (q8_0 V
+    // rows have the K geometry and share the K offsets.)
     const int klead = WIDE ? (g * CB) & 15 : 0;
     const int vlead = WIDE ? (g * CBV) & 15 : 0;
     constexpr int KO = WIDE ? KW : KN, VO = WIDE ? VW : VN;
@@ -530,7 +480,6 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         for (int m = 0; m < KO; ++m) voff[m] = koff[m];
     }
     uint32_t rk[WIDE ? 4 * KW : KN], rv[WIDE ? 4 * VW : VN];
-    // issue the loads of the sub-tile at row r0
     auto issue = [&](int r0) {
         const __amdgpu_buffer_rsrc_t kr = sub_rsrc(SG.k, SG.stride, SG.n_rows, CB, g, klead, r0);
         const __amdgpu_buffer_rsrc_t vr = sub_rsrc(SG.v, SG.vstride, SG.n_rows, CBV, g, vlead, r0);
@@ -543,17 +492,21 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         }
     };
     issue(r_begin + wave * R);
-    float Q[G][2];
+    float qv[NB][8];
     {
-        const float* qg = q + ((size_t)s * n_head_q + (size_t)g * G) * D + 32 * b + li;
+        // q of head n at dims 32 b + 8 gq .. + 7 (zero for the padding columns)
+        const bool real = n < G;
+        const float* qp = q + ((size_t)s * n_head_q + (size_t)g * G + (real ? n : 0)) * D + 8 * gq;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            Q[h][0] = qg[h * D];
-            Q[h][1] = qg[h * D + 16];
+        for (int b = 0; b < NB; ++b) {
+            const float4 a = *(const float4*)(qp + 32 * b);
+            const float4 c = *(const float4*)(qp + 32 * b + 4);
+            qv[b][0] = a.x, qv[b][1] = a.y, qv[b][2] = a.z, qv[b][3] = a.w;
+            qv[b][4] = c.x, qv[b][5] = c.y, qv[b][6] = c.z, qv[b][7] = c.w;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qv[b][j] = real ? qv[b][j] : 0.f;
         }
     }
-    // The arguments that were not preloaded, read (and waited for) while the
-    // first sub-tile is in flight.
     const int32_t n_vis = A.seq[s].seg[seg].n_vis, seq_splits = A.seq[s].n_split, split_off = A.split_off;
     const float scale_log2e = A.scale_log2e;
     float* const out = A.out;
@@ -570,41 +523,58 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
     const bool single = seq_splits == 1;
     const int abs_split = split_off + lsplit;
 
+    // the query in log2 units, scaled by a power of two per head, as two binary16 parts
+    half8_t qh[NB], ql[NB];
+    float unscale, rescale;  // 2^(E - 15) and 2^(15 - E) for head n
+    {
+        float amax = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qv[b][j] *= scale_log2e;
+                amax = fmaxf(amax, fabsf(qv[b][j]));
+            }
+        }
+        amax = fmaxf(amax, xchg16(amax));
+        amax = fmaxf(amax, xchg32(amax, lane));
+        int e = __builtin_amdgcn_frexp_expf(amax);  // amax = f 2^e, f in [0.5, 1); 0 for 0, inf, nan
+        e = min(max(e, -100), 120);
+        rescale = __builtin_ldexpf(1.f, 15 - e);
+        unscale = __builtin_ldexpf(1.f, e - 15);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float x = qv[b][j] * rescale;
+                const _Float16 hi = (_Float16)x;
+                qh[b][j] = hi;
+                ql[b][j] = (_Float16)(x - (float)hi);
+            }
+        }
+    }
+
     uint32_t* const tk = s_lds[wave];
     uint32_t* const tv = s_lds[wave] + WL::K;
-    // LDS addresses of this lane's K window (block b of row rho): the scale
-    // dword, and the 9 dwords from which the 32 codes are realigned (an odd
-    // block's codes start one dword later, dword-aligned; an even block's two
-    // bytes into its first dword).  The leads are multiples of 4 bytes.
-    const int kwin = rho * PK + (klead >> 2) + ((34 * b) >> 2);
-    const uint32_t* const kscale_p = tk + kwin;
-    const uint32_t* const kcode_p = tk + kwin + odd;
-    const int kshift = odd ? 0 : 2;
-    const uint32_t* const vscale_p = tv + rho * PV + (vlead >> 2) + ((L_::VB * b) >> 2);
-    // the lane's V values of row 0 of its row set (rows follow PV dwords apart)
-    const uint8_t* const vcode_p = (const uint8_t*)(tv + 16 * (dr / NB) * PV) + vlead + L_::VB * b + 2 +
-                                   (VT ? li : 2 * li);
 
-    float m[G], l[G], o[G][2], cs[G];
+    float m = -INFINITY, l = 0.f, thr = -INFINITY;
+    float cs[NB];  // q4_0: sum of the weights per block
+    float4_t o[NB][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        m[h] = -INFINITY;
-        l[h] = 0.f;
-        cs[h] = 0.f;
-        o[h][0] = o[h][1] = 0.f;
+    for (int b = 0; b < NB; ++b) {
+        cs[b] = 0.f;
+        o[b][0] = o[b][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
     }
-    dpp_source_guard(Q);
 
-    for (int t = wave; t < n_sub; t += 4) {
+    for (int t = wave; t < n_sub; t += W) {
         const int row0 = r_begin + t * R;
         const int nv = min(R, r_end - row0);
         {
             // Issue priority grows with the sub-tiles this wave has left.  The
-            // SIMD otherwise favours its oldest waves: the first workgroups
-            // placed on a CU ran ahead and finished early (by per-workgroup
-            // timestamps, 64 us against 103 us for the last ones at 131072
-            // rows), leaving the last ones to run at low occupancy.
-            const int rem = (n_sub - t + 3) >> 2;
+            // SIMD otherwise favours its oldest waves, and the first
+            // workgroups placed on a CU ran ahead and finished early, leaving
+            // the last ones to run at low occupancy.
+            const int rem = (n_sub - t + W - 1) / W;
             if (rem > 8)
                 __builtin_amdgcn_s_setprio(3);
             else if (rem > 4)
@@ -621,142 +591,159 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             store_narrow<KN>(rk, tk, lane);
             store_narrow<VN>(rv, tv, lane);
         }
-        if (t + 4 < n_sub) issue(row0 + 4 * R);
+        if (t + W < n_sub) issue(row0 + W * R);
         wave_lds_sync();
 
-        // ---- scores of (row rho, block b), summed over the blocks of the row
-        float sc[G];
-        {
-            uint32_t z[9];
 #pragma unroll
-            for (int j = 0; j < 9; ++j) z[j] = kcode_p[j];
-            const uint32_t kd = *kscale_p;
-            uint32_t cw[8];
+        for (int rs = 0; rs < RS; ++rs) {
+            // ---- scores of rows 16 rs + 4 gq + j, head n
+            float sc[4];
+            {
+                const uint32_t* const kc = tk + (16 * rs + n) * PK + (klead >> 2) + 2 * gq;
+                const uint32_t* const ks = tk + (16 * rs + 4 * gq) * PK + (klead >> 2);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) cw[k] = __builtin_amdgcn_alignbyte(z[k + 1], z[k], kshift);
-            float dot[G];
-            ScoreCodes<G, 0>::run(dot, Q, cw);
-            const float dk = half_lo(kd >> (16 * odd)) * scale_log2e;
+                for (int b = 0; b < NB; ++b) {
+                    // block b: scale at byte 34 b, codes from byte 34 b + 2
+                    const uint32_t* const zp = kc + ((34 * b + 2) >> 2);
+                    const half8_t a = (b & 1) ? kcodes_f16<0>(zp) : kcodes_f16<2>(zp);
+                    float4_t acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ql[b], (float4_t){0.f, 0.f, 0.f, 0.f},
+                                                                          0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qh[b], acc, 0, 0, 0);
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                // the product is rounded before the exchange (the empty asm keeps
-                // the compiler from fusing it into the add), so every lane of a
-                // row adds the same two rounded values and holds the same score
-                float x = dot[h] * dk;
-                asm("" : "+v"(x));
-                x += xchg16(x);
-                if constexpr (NB == 4) x += xchg32(x, lane);
-                sc[h] = x;
-            }
-        }
-        if (nv < R) {
-            // only a split's last sub-tile can be partial
-#pragma unroll
-            for (int h = 0; h < G; ++h) sc[h] = (rho < nv) ? sc[h] : -INFINITY;
-        }
-
-        // ---- online softmax (wave-uniform running maximum per head)
-        if (t == wave) {
-            // first sub-tile of the wave: start from the score of its first row
-            // (always visible); the lazy rule below still raises it
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-                m[h] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sc[h])));
-        }
-        {
-            bool big = false;
-#pragma unroll
-            for (int h = 0; h < G; ++h) big |= sc[h] > m[h] + kLazyMax;
-            if (__builtin_amdgcn_ballot_w64(big)) {
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float mn = fmaxf(m[h], wave_max(sc[h]));
-                    if (mn > m[h]) {
-                        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
-                        l[h] *= alpha;
-                        if (VT) cs[h] *= alpha;
-                        o[h][0] *= alpha;
-                        o[h][1] *= alpha;
-                        m[h] = mn;
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w = ks[j * PK + ((34 * b) >> 2)];
+                        const float dk = (b & 1) ? f16_half<1>(w) : f16_half<0>(w);
+                        sc[j] = (b == 0) ? dk * acc[j] : fmaf(dk, acc[j], sc[j]);
                     }
                 }
             }
-        }
-        float c[G];
-        {
-            // rows past the visible range may hold any bits: their coefficient is an exact 0
-            const uint32_t vd = *vscale_p;
-            const float dv = (rho < nv) ? half_lo(vd >> (16 * odd)) : 0.f;
+            if (nv < R) {
+                // only a split's last sub-tile can be partial
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
-                l[h] += p;
-                c[h] = p * dv;
-                if (VT) cs[h] += c[h];
+                for (int j = 0; j < 4; ++j) sc[j] = (16 * rs + 4 * gq + j < nv) ? sc[j] : -INFINITY;
+            }
+            // ---- online softmax
+            {
+                const float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                if (__builtin_amdgcn_ballot_w64(smax > thr)) {
+                    float x = fmaxf(smax, xchg16(smax));
+                    x = fmaxf(x, xchg32(x, lane));
+                    const float mn = fmaxf(m, x * unscale);
+                    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+                    l *= alpha;
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        if (VT) cs[b] *= alpha;
+                        o[b][0] *= alpha;
+                        o[b][1] *= alpha;
+                    }
+                    m = mn;
+                    thr = (m + kLazyMax) * rescale;
+                }
+            }
+            float p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                p[j] = __builtin_amdgcn_exp2f(fmaf(sc[j], unscale, -m));
+                l += p[j];
+            }
+            // ---- values
+            const uint32_t* const vs = tv + (16 * rs + 4 * gq) * PV + (vlead >> 2);
+            const uint8_t* const vc =
+                (const uint8_t*)(tv + (16 * rs + 4 * gq) * PV) + vlead + 2 + (VT ? n : 2 * n);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float x[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t w = vs[j * PV + ((VB * b) >> 2)];
+                    const float dv = (b & 1) ? f16_half<1>(w) : f16_half<0>(w);
+                    x[j] = p[j] * dv;
+                }
+                if (nv < R) {
+                    // rows past the visible range may hold any bits: their weight is an exact 0
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x[j] = (16 * rs + 4 * gq + j < nv) ? x[j] : 0.f;
+                }
+                if constexpr (VT) cs[b] += (x[0] + x[1]) + (x[2] + x[3]);
+                // the weights as bfloat16 hi + lo parts
+                const uint32_t h01 = bf16_pair(x[0], x[1]), h23 = bf16_pair(x[2], x[3]);
+                const uint32_t l01 = bf16_pair(x[0] - __builtin_bit_cast(float, h01 << 16),
+                                               x[1] - __builtin_bit_cast(float, h01 & 0xffff0000u));
+                const uint32_t l23 = bf16_pair(x[2] - __builtin_bit_cast(float, h23 << 16),
+                                               x[3] - __builtin_bit_cast(float, h23 & 0xffff0000u));
+                const short4_t wh = __builtin_bit_cast(short4_t, (uint2){h01, h23});
+                const short4_t wl = __builtin_bit_cast(short4_t, (uint2){l01, l23});
+                float f[2][4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (VT == 0) {
+                        uint32_t y = *(const uint16_t*)(vc + j * 4 * PV + VB * b);
+                        asm("" : "+v"(y));
+                        f[0][j] = (float)(int8_t)y;
+                        f[1][j] = (float)(int8_t)(y >> 8);
+                    } else {
+                        uint32_t y = vc[j * 4 * PV + VB * b];
+                        asm("" : "+v"(y));
+                        f[0][j] = (float)(y & 15u);
+                        f[1][j] = (float)(uint8_t)y;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const short4_t a =
+                        __builtin_bit_cast(short4_t, (uint2){bf16_pair(f[c][0], f[c][1]), bf16_pair(f[c][2], f[c][3])});
+                    o[b][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, wl, o[b][c], 0, 0, 0);
+                    o[b][c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, wh, o[b][c], 0, 0, 0);
+                }
             }
         }
-        dpp_source_guard(c);
-
-        // ---- values: the 16 rows of the lane's row set, coefficients broadcast from lane n
-        ValueRows<G, VT, 0>::run(o, c, vcode_p, 4 * PV);
         wave_lds_sync();
     }
 
     // ---- this wave's (m, l, o) to its LDS area, then the four waves merge
-    // l: every lane of a row holds its p, so count block 0's lanes only
-#pragma unroll
-    for (int h = 0; h < G; ++h) l[h] = wave_sum(b == 0 ? l[h] : 0.f);
+    l += xchg16(l);
+    l += xchg32(l, lane);
     if constexpr (VT) {
-        // sum of the coefficients over the rows of the lane's block
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            cs[h] = row16_sum(cs[h]);
-            if constexpr (NB == 2) cs[h] += xchg32(cs[h], lane);
-        }
-    }
-    if constexpr (NB == 2) {
-        // two row sets: their partial sums meet
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            o[h][0] += xchg32(o[h][0], lane);
-            o[h][1] += xchg32(o[h][1], lane);
+        for (int b = 0; b < NB; ++b) {
+            cs[b] += xchg16(cs[b]);
+            cs[b] += xchg32(cs[b], lane);
         }
     }
     float* const mw = (float*)s_lds[wave];  // m [G], l [G], o [G][D]
-    if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            mw[h] = m[h];
-            mw[G + h] = l[h];
+    if (n < G) {
+        if (gq == 0) {
+            mw[n] = m;
+            mw[G + n] = l;
         }
-    }
-    if (dr < NB) {
-        // one row set holds the wave's sums: dims of this lane
-        const int d0 = VT ? 32 * b + li : 32 * b + 2 * li;
-        const int d1 = VT ? d0 + 16 : d0 + 1;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float a0 = o[h][0], a1 = o[h][1];
-            if constexpr (VT) {
-                // low nibbles and whole bytes -> dims i and i + 16, codes offset by 8
-                const float hi = (a1 - a0) * 0.0625f;
-                a0 = a0 - 8.f * cs[h];
-                a1 = hi - 8.f * cs[h];
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = 4 * gq + j;  // MFMA row of the result
+                if constexpr (VT == 0) {
+                    mw[2 * G + n * D + 32 * b + 2 * i] = o[b][0][j];
+                    mw[2 * G + n * D + 32 * b + 2 * i + 1] = o[b][1][j];
+                } else {
+                    // low nibbles and whole bytes -> dims i and i + 16, codes offset by 8
+                    const float lo = o[b][0][j], hi = (o[b][1][j] - lo) * 0.0625f;
+                    mw[2 * G + n * D + 32 * b + i] = lo - 8.f * cs[b];
+                    mw[2 * G + n * D + 32 * b + 16 + i] = hi - 8.f * cs[b];
+                }
             }
-            mw[2 * G + h * D + d0] = a0;
-            mw[2 * G + h * D + d1] = a1;
         }
     }
     __syncthreads();
     const int hq0 = g * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
         const int h = idx / D, d = idx - h * D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, ((const float*)s_lds[w])[h]);
+        for (int w = 0; w < W; ++w) M = fmaxf(M, ((const float*)s_lds[w])[h]);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < W; ++w) {
             const float* mw2 = (const float*)s_lds[w];
             const float mk = mw2[h];
             const float a = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
@@ -917,30 +904,41 @@ typedef void (*combine_fn)(int32_t, int32_t, int32_t, const float*, const float*
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
-template <int D, int VT, int WIDE>
+template <int D, int VT, int WIDE, int W>
 decode_fn pick_decode_g(int G) {
     switch (G) {
-        case 1: return decode_kernel<D, 1, VT, WIDE>;
-        case 2: return decode_kernel<D, 2, VT, WIDE>;
-        case 3: return decode_kernel<D, 3, VT, WIDE>;
-        case 4: return decode_kernel<D, 4, VT, WIDE>;
-        case 5: return decode_kernel<D, 5, VT, WIDE>;
-        case 6: return decode_kernel<D, 6, VT, WIDE>;
-        case 7: return decode_kernel<D, 7, VT, WIDE>;
-        case 8: return decode_kernel<D, 8, VT, WIDE>;
+        case 1: return decode_kernel<D, 1, VT, WIDE, W>;
+        case 2: return decode_kernel<D, 2, VT, WIDE, W>;
+        case 3: return decode_kernel<D, 3, VT, WIDE, W>;
+        case 4: return decode_kernel<D, 4, VT, WIDE, W>;
+        case 5: return decode_kernel<D, 5, VT, WIDE, W>;
+        case 6: return decode_kernel<D, 6, VT, WIDE, W>;
+        case 7: return decode_kernel<D, 7, VT, WIDE, W>;
+        case 8: return decode_kernel<D, 8, VT, WIDE, W>;
     }
     return nullptr;
 }
 
-template <int WIDE>
+template <int WIDE, int W>
 decode_fn pick_decode_w(int D, int G, int VT) {
-    if (VT) return D == 128 ? pick_decode_g<128, 1, WIDE>(G) : pick_decode_g<64, 1, WIDE>(G);
-    return D == 128 ? pick_decode_g<128, 0, WIDE>(G) : pick_decode_g<64, 0, WIDE>(G);
+    if (VT) return D == 128 ? pick_decode_g<128, 1, WIDE, W>(G) : pick_decode_g<64, 1, WIDE, W>(G);
+    return D == 128 ? pick_decode_g<128, 0, WIDE, W>(G) : pick_decode_g<64, 0, WIDE, W>(G);
 }
 
-// wide: every K/V base and row stride of the call is a multiple of 16 bytes
-decode_fn pick_decode(int D, int G, int VT, bool wide) {
-    return wide ? pick_decode_w<1>(D, G, VT) : pick_decode_w<0>(D, G, VT);
+template <int W>
+decode_fn pick_decode_waves(int D, int G, int VT, bool wide) {
+    return wide ? pick_decode_w<1, W>(D, G, VT) : pick_decode_w<0, W>(D, G, VT);
+}
+
+// wide: every K/V base and row stride of the call is a multiple of 16 bytes;
+// waves: 4, 8 or 12 per workgroup
+decode_fn pick_decode(int D, int G, int VT, bool wide, int waves) {
+    switch (waves) {
+        case 4: return pick_decode_waves<4>(D, G, VT, wide);
+        case 8: return pick_decode_waves<8>(D, G, VT, wide);
+        case 12: return pick_decode_waves<12>(D, G, VT, wide);
+    }
+    return nullptr;
 }
 
 }  // namespace
@@ -994,6 +992,18 @@ extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* byt
     return KVD_OK;
 }
 
+extern "C" int kvd_attend_plan(const kvd_attn_args* args, int32_t* split_rows, int32_t* waves,
+                               int64_t* total_splits) {
+    clear_error();
+    AttendPlan p;
+    const int rc = plan_attend(args, &p, device_cus());
+    if (rc != KVD_OK) return rc;
+    if (split_rows) *split_rows = p.split_rows;
+    if (waves) *waves = p.waves;
+    if (total_splits) *total_splits = p.total_splits;
+    return KVD_OK;
+}
+
 namespace kvd {
 namespace {
 
@@ -1018,7 +1028,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
         if (g.n_rows > 0 && (((uintptr_t)g.k | (uintptr_t)g.v) % 16 || g.row_stride % 16 || vs % 16)) wide = false;
     }
-    const decode_fn dk = pick_decode(a->head_dim, p.group, a->v_type, wide);
+    const decode_fn dk = pick_decode(a->head_dim, p.group, a->v_type, wide, p.waves);
     const combine_fn ck = pick_combine(a->head_dim);
     if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
 
@@ -1077,7 +1087,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         L.scale_log2e = scale_log2e;
         const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);  // the kernel assumes this rounding
         const SegDesc& f = L.seq[0].seg[0];
-        hipLaunchKernelGGL(dk, dim3(grid), dim3(256), 0, (hipStream_t)stream, L.n_items,
+        hipLaunchKernelGGL(dk, dim3(grid), dim3(64 * p.waves), 0, (hipStream_t)stream, L.n_items,
                            L.n_head_kv | (L.n_seq << 16), L.split_rows, f.n_split, L.q, f.k, f.v, f.stride, f.vstride,
                            f.row_lo, f.n_rows, L);
         hipError_t e = hipGetLastError();

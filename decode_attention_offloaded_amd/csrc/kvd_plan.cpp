@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <vector>
 
 namespace kvd {
 namespace {
@@ -20,35 +21,72 @@ int64_t slice_workgroups(const AttendPlan& p, int n_head_kv, int64_t rows) {
     return wgs * n_head_kv;
 }
 
-// Relative time per unit of work when the busiest CU runs `per_cu` workgroups:
-// one workgroup per CU (one wave per SIMD) hides little latency; up to four
-// are resident at once (registers and LDS allow four), beyond that they queue.
-int64_t slice_occupancy_cost(int64_t per_cu) {
-    return per_cu == 1 ? 160 : per_cu == 2 ? 100 : per_cu == 3 ? 93 : 87;
+// 16-row sub-tiles of every (visible range, KV head), per CU: the work the
+// chip shares out, in the unit a wave computes at a time.
+int64_t subtiles_per_cu(const AttendPlan& p, int n_head_kv, int64_t n_cus) {
+    int64_t u = 0;
+    for (const SeqPlan& sp : p.seq) u += ceil_div(sp.seg[0].n_vis, 16) + ceil_div(sp.seg[1].n_vis, 16);
+    return u * n_head_kv / n_cus;
 }
 
-// Tiles (64 rows) per split for the block-sliced kernel, all waves of a
-// workgroup sharing each tile.  A candidate of k tiles gives W workgroups; the
-// busiest CU then runs ceil(W / CUs) of them, each costing k tiles plus
-// kSliceOverheadTiles of fixed work (start-up, fold, partial write), weighted
-// by slice_occupancy_cost.  The cheapest candidate wins, the larger on a tie.
-// On one sequence of 1024 ... 131072 rows x 8 KV heads this picks the
-// measured fastest split or one within 1%.
-int64_t slice_tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis, int64_t n_cus) {
+// Waves per workgroup for a given amount of work per CU.  The decode kernel
+// holds three waves per SIMD (its register count); a long context runs best
+// as one workgroup of 12 waves per CU (the split's online-softmax states merge
+// once per CU, and the combine has the fewest partials), a medium one as one
+// of 8, and a short one (a few sub-tiles per CU) as several of 4, whose
+// waves each get more sub-tiles to overlap their loads with.  Measured on
+// MI355X over 4096 ... 131072 rows x 8 KV heads.
+int plan_waves(int64_t subtiles) {
+    return subtiles >= kWaves12Subtiles ? 12 : subtiles >= kWaves8Subtiles ? 8 : 4;
+}
+
+// Relative time per unit of work of a 4-wave workgroup when the busiest CU
+// runs `per_cu` of them: one per CU (one wave per SIMD) hides little latency;
+// up to kWavesPerSimd are resident at once, beyond that they queue in rounds.
+int64_t occupancy_cost(int64_t per_cu) {
+    const int64_t resident = kWavesPerSimd;
+    const int64_t eff = per_cu <= resident ? per_cu : resident * ceil_div(per_cu, resident);
+    const int64_t occ = per_cu == 1 ? 160 : per_cu == 2 ? 100 : 93;
+    return occ * eff;
+}
+
+// Tiles (64 rows) per split.  A candidate of k tiles gives a number of
+// workgroups; the busiest CU then runs ceil(workgroups / CUs) of them, each
+// costing k tiles plus a fixed amount of work (start-up, merge, partial
+// write).  4-wave workgroups weigh that by occupancy_cost; the 8- and 12-wave
+// ones run one at a time per CU, so the cost is the number of rounds times
+// (k + kBigOverheadTiles).  Candidates: every k up to 16, then steps of about
+// 25%, and for r = 1 .. 4 the smallest k that gives at most r workgroups per
+// CU.  The cheapest wins, the larger on a tie.
+int64_t tiles_per_split(const AttendPlan& p, int n_head_kv, int64_t max_vis, int64_t n_cus, int waves) {
     const int64_t max_k = std::max<int64_t>(1, ceil_div(max_vis, kTileRows));
+    auto per_cu = [&](int64_t k) { return ceil_div(slice_workgroups(p, n_head_kv, k * kTileRows), n_cus); };
+    std::vector<int64_t> cand;
+    for (int64_t k = 1; k <= max_k; k = k < 16 ? k + 1 : k + k / 4) cand.push_back(k);
+    cand.push_back(max_k);
+    for (int64_t r = 1; r <= 4; ++r) {
+        // workgroups fall as k grows: bisect for the first k with per_cu(k) <= r
+        int64_t lo = 1, hi = max_k;
+        if (per_cu(hi) > r) continue;
+        while (lo < hi) {
+            const int64_t mid = lo + (hi - lo) / 2;
+            if (per_cu(mid) <= r)
+                hi = mid;
+            else
+                lo = mid + 1;
+        }
+        cand.push_back(lo);
+    }
+    std::sort(cand.begin(), cand.end());
     int64_t best_k = 1, best_cost = INT64_MAX;
-    for (int64_t k = 1; k <= max_k;) {
-        const int64_t per_cu = ceil_div(slice_workgroups(p, n_head_kv, k * kTileRows), n_cus);
-        const int64_t cost = slice_occupancy_cost(per_cu) * per_cu * (k + kSliceOverheadTiles);
+    for (const int64_t k : cand) {
+        const int64_t pc = per_cu(k);
+        const int64_t cost =
+            waves == 4 ? occupancy_cost(pc) * (k + kSliceOverheadTiles) : pc * (k + kBigOverheadTiles);
         if (cost <= best_cost) {
             best_cost = cost;
             best_k = k;
-        } else if (per_cu == 1) {
-            break;  // one workgroup per CU already: larger k only costs more
         }
-        // every k up to 16, then steps of about 25%
-        const int64_t next = k < 16 ? k + 1 : k + k / 4;
-        k = (k < max_k && next > max_k) ? max_k : next;
     }
     return best_k;
 }
@@ -154,9 +192,10 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus) {
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
     p->n_cus = n_cus;
+    p->waves = plan_waves(subtiles_per_cu(*p, a->n_head_kv, n_cus));
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
-        split_rows = (int64_t)kTileRows * slice_tiles_per_split(*p, a->n_head_kv, max_vis, n_cus);
+        split_rows = (int64_t)kTileRows * tiles_per_split(*p, a->n_head_kv, max_vis, n_cus, p->waves);
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kTileRows) * kTileRows;
         split_rows = std::max(split_rows, floor_rows);

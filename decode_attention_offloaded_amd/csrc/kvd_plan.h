@@ -14,7 +14,11 @@ constexpr int kTileRows = 64;           // rows per tile of the decode kernel (s
 constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
 constexpr int kDefaultCUs = 256;          // MI355X compute units, when the device cannot be asked
-constexpr int64_t kSliceOverheadTiles = 3;  // block-sliced fixed work per workgroup, in tiles
+constexpr int64_t kSliceOverheadTiles = 3;  // fixed work of a 4-wave workgroup, in tiles
+constexpr int64_t kBigOverheadTiles = 6;    // fixed work of an 8- or 12-wave workgroup, in tiles
+constexpr int kWavesPerSimd = 3;            // decode-kernel waves resident per SIMD (registers)
+constexpr int64_t kWaves8Subtiles = 24;     // sub-tiles per CU from which 8-wave workgroups are used
+constexpr int64_t kWaves12Subtiles = 96;    // ... and 12-wave ones
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
 
 struct SegPlan {
@@ -36,6 +40,7 @@ struct AttendPlan {
     int32_t chunk_bytes;  // bytes of one head of one row: head_dim / 32 * 34
     int32_t split_rows;
     int32_t n_cus;        // compute units the plan was made for
+    int32_t waves;        // waves per decode workgroup: 4, 8 or 12
     int32_t max_splits;   // largest per-sequence split count
     int64_t total_splits;
     std::vector<SeqPlan> seq;

@@ -88,6 +88,9 @@ def _declare(L):
     L.kvd_link_probe.argtypes = [c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
     L.kvd_attend_workspace_bytes.restype = c_int
     L.kvd_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(c_size_t)]
+    L.kvd_attend_plan.restype = c_int
+    L.kvd_attend_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     L.kvd_attend_decode.restype = c_int
     L.kvd_attend_decode.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
     L.kvd_attend_decode_noalloc.restype = c_int
@@ -217,6 +220,13 @@ def workspace_bytes(args: AttnArgs) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().kvd_attend_workspace_bytes(ctypes.byref(args), ctypes.byref(n)))
     return int(n.value)
+
+
+def attend_plan(args: AttnArgs):
+    """(rows per split, waves per decode workgroup, total splits) of a call."""
+    sr, w, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(lib().kvd_attend_plan(ctypes.byref(args), ctypes.byref(sr), ctypes.byref(w), ctypes.byref(ns)))
+    return int(sr.value), int(w.value), int(ns.value)
 
 
 class Workspace:

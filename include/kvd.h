@@ -158,6 +158,15 @@ typedef struct kvd_attn_args {
  * order the streams). */
 int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
 
+/* The launch plan a call with these arguments gets on the current device,
+ * without launching anything (validates the arguments too): rows per split,
+ * waves per decode workgroup (4, 8 or 12, chosen from the work per compute
+ * unit) and the splits of all sequences together.  Any output pointer may be
+ * NULL.  Returns KVD_OK or KVD_EINVAL.  The plan depends on the shapes and the
+ * device's compute-unit count only ("F5 -- Advanced KV Cache Techniques", M4:
+ * split-K decode over row ranges, merged by running maxima and sums). */
+int kvd_attend_plan(const kvd_attn_args* args, int32_t* split_rows, int32_t* waves, int64_t* total_splits);
+
 /* Enqueue decode attention on `stream` (asynchronous).  Returns KVD_OK,
  * KVD_EINVAL (bad shapes, unaligned or null pointers, a sequence with no
  * visible row, workspace too small) or KVD_EHIP (launch failure). */

@@ -115,19 +115,38 @@ def _splits(n_rows_list, seg_rows=None):
     return s
 
 
-@pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (16384, 64), (32768, 64),
-                                      (65536, 64), (131072, 128)])
+@pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (12288, 32), (16384, 32),
+                                      (32768, 32), (65536, 32), (131072, 32)])
 def test_split_plan_single_sequence(n, splits):
-    """Splits per KV head on one sequence of n rows x 8 KV heads (the measured
-    fastest or within 2% of it: 64-row splits up to 2048 rows, then two
-    workgroups per CU up to 65536 rows, four at 131072 rows)."""
+    """Splits per KV head on one sequence of n rows x 8 KV heads on 256 CUs
+    (the measured fastest, or within 2% of it): 64-row splits up to 2048 rows,
+    128-row ones at 4096 and 8192 rows (4-wave workgroups, one or two per
+    CU), then one 8- or 12-wave workgroup per CU, 32 splits per head."""
     assert _splits([n]) == splits
 
 
+@pytest.mark.parametrize("n,split_rows,waves", [(256, 256, 4), (4096, 128, 4), (8192, 128, 4), (12288, 384, 8),
+                                                 (16384, 512, 8), (49152, 1536, 12), (131072, 4096, 12)])
+def test_planned_waves(n, split_rows, waves):
+    """Rows per split and waves per decode workgroup on 256 CUs, one sequence
+    of n rows x 8 KV heads: 4-wave workgroups below 24 sub-tiles of 16 rows
+    per CU, 8-wave ones below 96, then 12-wave ones (one per CU)."""
+    a, _ = _args()
+    a.segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, n, 0, 1088))
+    sr, w, total = kvd.attend_plan(a)
+    assert (sr, w) == (split_rows, waves)
+    assert total == -(-n // sr)
+    bad, _ = _args()
+    bad.head_dim = 96
+    assert kvd.lib().kvd_attend_plan(ctypes.byref(bad), None, None, None) == kvd.KVD_EINVAL
+    assert kvd.lib().kvd_attend_plan(ctypes.byref(a), None, None, None) == kvd.KVD_OK
+
+
 def test_split_plan_batch():
-    """16 sequences in two segments each: 768-row splits, so 120 in all."""
+    """16 sequences in two segments each (84227 rows in all, so 12-wave
+    workgroups): 1664-row splits, 64 in all, two workgroups per CU."""
     lens = [1024, 1024, 1862, 1990, 2813, 3712, 3769, 4264, 5376, 5801, 6363, 6588, 7292, 8678, 9634, 10041]
-    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 768) + -(-(n - n // 2) // 768) for n in lens) == 120
+    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 1664) + -(-(n - n // 2) // 1664) for n in lens) == 64
 
 
 def test_workspace_too_small_is_rejected():

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from decode_attention_offloaded_amd import inputs
-from tests.helpers import gpu_attend, head_slice, make_cache
+from tests.helpers import gpu_attend, head_slice, make_cache, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -166,11 +166,10 @@ def test_long_context_sampled_heads(oracle):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("g_size", [1, 2, 4, 8])
 def test_long_range_every_group_size(oracle, d, g_size):
-    """One range of 65600 rows x 8 KV heads (ragged last tile), three ways:
-    as planned (several workgroups per CU, so groups of up to 5 take the
-    query by scalar loads), in 2112-row splits (32 per KV head: one workgroup
-    per CU, the query from LDS), and in two segments.  Sampled KV heads of each against
-    the oracle, for every GQA group size the kernel is built for."""
+    """One range of 65600 rows x 8 KV heads (ragged last sub-tile), three
+    ways: as planned (one 12-wave workgroup per CU), in 2112-row splits (32
+    per KV head) and in two segments.  Sampled KV heads of each against the
+    oracle, for group sizes 1 (15 padding columns in every MFMA) up to 8."""
     n, hkv = 65600, 8
     hq = hkv * g_size
     rng, k, v = make_cache(7000 + d + g_size, n, hkv, d)
@@ -183,6 +182,39 @@ def test_long_range_every_group_size(oracle, d, g_size):
         ks, vs = head_slice(k, g, hkv, d), head_slice(v, g, hkv, d)
         ref = oracle.attend(q[:, g * g_size:(g + 1) * g_size], [[(ks, vs, 0)]], 1, d, threads=8)
         for out in (one, wide, two):
+            check(out[:, g * g_size:(g + 1) * g_size], ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("v_type", [0, 1])
+def test_eight_wave_workgroups(oracle, d, v_type):
+    """20001 rows x 8 KV heads: enough work per CU for 8-wave workgroups (one
+    per CU), q8_0 and q4_0 V, as planned, in 640-row splits and in two
+    segments; sampled KV heads against the oracle."""
+    from decode_attention_offloaded_amd import kvd
+    n, hkv, g_size = 20001, 8, 5
+    hq = hkv * g_size
+    rng = np.random.default_rng(8100 + d + v_type)
+    k = inputs.random_kv_rows(rng, n, hkv, d)
+    v = inputs.random_kv_rows_q4_0(rng, n, hkv, d) if v_type else inputs.random_kv_rows(rng, n, hkv, d)
+    q = inputs.random_q(rng, 1, hq, d)
+    import torch
+    qd = to_dev(q)
+    h = n // 3
+    outs = []
+    for segs, sr in (([(k, v, 0)], 0), ([(k, v, 0)], 640), ([(k[:h], v[:h], 0), (k[h:], v[h:], h)], 0)):
+        out = torch.full_like(qd, float("nan"))
+        kvd.attend_decode(qd, out, [[(to_dev(a), to_dev(b), p0) for (a, b, p0) in segs]], hkv, split_rows=sr,
+                          v_type=v_type)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    kcb, vcb = d // 32 * 34, d // 32 * (18 if v_type else 34)
+    for g in (0, 6):
+        ks = np.ascontiguousarray(k[:, g * kcb:(g + 1) * kcb])
+        vs = np.ascontiguousarray(v[:, g * vcb:(g + 1) * vcb])
+        ref = oracle.attend(q[:, g * g_size:(g + 1) * g_size], [[(ks, vs, 0)]], 1, d, threads=8,
+                            v_type=oracle.V_Q4_0 if v_type else oracle.V_Q8_0)
+        for out in outs:
             check(out[:, g * g_size:(g + 1) * g_size], ref)
 
 
@@ -238,9 +270,9 @@ def test_graph_replays_match_eager(n, v_type):
 
 def test_workspace_grows_eagerly_and_under_capture():
     """A workspace sized by a short call grows for larger ones: between eager
-    calls (after a device wait: 1024 rows, then 16384) and during graph
-    capture (keeping the old buffer: 16384 rows with 64 query heads, more
-    partials per split).  Outputs equal those of calls with a fresh
+    calls (after a device wait: 1024 rows in 16 splits per KV head, then 8192
+    rows in 64) and during graph capture (keeping the old buffer: 8192 rows
+    with 64 query heads, more partials per split).  Outputs equal those of calls with a fresh
     workspace of their own, and the captured call replays to the same bytes."""
     import torch
     from decode_attention_offloaded_amd import kvd
@@ -251,7 +283,7 @@ def test_workspace_grows_eagerly_and_under_capture():
         vd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
         return torch.from_numpy(inputs.random_q(rng, 1, hq, 128)).cuda(), [[(kd, vd, 0)]]
 
-    calls = [cache(1024, 40), cache(16384, 40), cache(16384, 64)]
+    calls = [cache(1024, 40), cache(8192, 40), cache(8192, 64)]
     refs = []
     for q, segs in calls:
         r = torch.empty_like(q)
@@ -298,7 +330,7 @@ def test_captured_workspace_survives_eager_growth():
         vd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
         return torch.from_numpy(inputs.random_q(rng, 1, 40, 128)).cuda(), [[(kd, vd, 0)]]
 
-    small, big = cache(2048), cache(32768)
+    small, big = cache(2048), cache(8192)   # 32 and 64 splits per KV head
     ref = torch.empty_like(small[0])
     kvd.attend_decode(small[0], ref, small[1], 8, workspace=kvd.Workspace())
     torch.cuda.synchronize()

@@ -46,9 +46,8 @@ def test_q4_v_matches_oracle(oracle, d, hq, hkv, n):
 
 @pytest.mark.parametrize("g_size", [5, 8])
 def test_q4_v_long_context_sampled_heads(oracle, g_size):
-    """131072 rows x 8 KV heads with q4_0 V (the block-sliced kernel at 32
-    tiles per split): sampled KV heads against the oracle run on that head's
-    bytes alone."""
+    """131072 rows x 8 KV heads with q4_0 V (one 12-wave workgroup per CU):
+    sampled KV heads against the oracle run on that head's bytes alone."""
     n, hkv, d = 131072, 8, 128
     hq = hkv * g_size
     rng, k, v = _cache(515 + g_size, n, hkv, d)
