@@ -81,7 +81,7 @@ def test_workspace_plan():
     a, _ = _args()
     n = kvd.workspace_bytes(a)
     # 4096 rows x 8 KV heads = 512 tiles of 64 rows: one workgroup per CU with
-    # two tiles each, i.e. 32 splits per head
+    # two tiles each, i.e. 32 splits per head (split maxima, sums, outputs)
     splits = 32
     expect = 2 * ((splits * 40 * 4 + 255) // 256 * 256) + splits * 40 * 128 * 4
     assert n == expect
@@ -93,8 +93,7 @@ def test_workspace_plan():
 
 
 def _splits(n_rows_list, seg_rows=None):
-    """Total splits the planner makes, read back from the workspace size
-    (2 x 256-byte-rounded m and l arrays + the o array, 40 heads x 128 dims)."""
+    """Total splits the planner makes (kvd_attend_plan), 40 query / 8 KV heads."""
     segs = []
     for n in n_rows_list:
         if seg_rows is None:
@@ -105,14 +104,7 @@ def _splits(n_rows_list, seg_rows=None):
     raw = (kvd.KvSeg * len(segs))(*segs)
     a, _ = _args(n_seq=len(n_rows_list), n_seg=1 if seg_rows is None else 2)
     a.segs = raw
-    nb = kvd.workspace_bytes(a)
-    if nb == 0:
-        return 1
-    s = max(0, (nb - 512) // (40 * 130 * 4))
-    while 2 * ((s * 160 + 255) // 256 * 256) + s * 40 * 128 * 4 < nb:
-        s += 1
-    assert 2 * ((s * 160 + 255) // 256 * 256) + s * 40 * 128 * 4 == nb
-    return s
+    return kvd.attend_plan(a)[2]
 
 
 @pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (12288, 32), (16384, 32),

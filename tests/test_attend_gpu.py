@@ -126,6 +126,38 @@ def test_batched_varlen_swa_two_segments(oracle):
         check(out, ref)
 
 
+def test_one_workspace_for_calls_of_every_shape(oracle):
+    """One workspace serves, in turn, a long single-sequence call, a
+    16-sequence call in two segments, a call with other head counts and the
+    first call again: whatever an earlier call left in it, each call's
+    partials are its own."""
+    from decode_attention_offloaded_amd import kvd
+    rng = np.random.default_rng(5150)
+    ws = kvd.Workspace()
+    calls = []
+    k, v = inputs.random_kv_rows(rng, 9000, 8, 128), inputs.random_kv_rows(rng, 9000, 8, 128)
+    calls.append((inputs.random_q(rng, 1, 40, 128), [[(k, v, 0)]], 8, 128))
+    lens = inputs.lognormal_lengths(rng, 16, median=700, sigma=0.8, lo=200, hi=3000)
+    segs = []
+    for n in lens:
+        kk, vv = inputs.random_kv_rows(rng, int(n), 8, 128), inputs.random_kv_rows(rng, int(n), 8, 128)
+        h = int(n) // 2
+        segs.append([(kk[:h], vv[:h], 0), (kk[h:], vv[h:], h)])
+    calls.append((inputs.random_q(rng, 16, 40, 128), segs, 8, 128))
+    k2, v2 = inputs.random_kv_rows(rng, 5000, 2, 64), inputs.random_kv_rows(rng, 5000, 2, 64)
+    calls.append((inputs.random_q(rng, 1, 16, 64), [[(k2, v2, 0)]], 2, 64))
+    calls.append(calls[0])
+    import torch
+    for q, sg, hkv, d in calls:
+        ref = oracle.attend(q, sg, hkv, d, threads=8)
+        qd = to_dev(q)
+        out = torch.full_like(qd, float("nan"))
+        kvd.attend_decode(qd, out, [[(to_dev(a), to_dev(b), p0) for (a, b, p0) in seq] for seq in sg], hkv,
+                          workspace=ws)
+        torch.cuda.synchronize()
+        check(out.cpu().numpy(), ref)
+
+
 def test_empty_first_segment_under_window(oracle):
     hq, hkv, d = 8, 2, 64
     rng, k, v = make_cache(11, 400, hkv, d)
