@@ -735,22 +735,52 @@ def traffic_source_sha():
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per call from the committed counter summary, or None when the
-    kernel or plan source has changed since the counters were taken."""
-    prof = os.path.join(ROOT, "profiles", "decode_attention_4096rows_hbm_traffic.md")
+def profile_fields(name):
+    """The machine-readable fields (indented `key: value` lines) of a committed
+    profile summary, or None when the kernel or plan source has changed since
+    its counters were taken (or the file is missing)."""
     try:
-        sha = traffic_source_sha()
         fields = {}
-        for line in open(prof):
+        for line in open(os.path.join(ROOT, "profiles", name)):
             if ":" in line and line.startswith("    "):
                 k, v = line.strip().split(":", 1)
                 fields[k.strip()] = v.strip()
-        if fields.get("source_sha256") == sha:
-            return int(fields["traffic_bytes_per_call"])
-    except (OSError, KeyError, ValueError):
+        if fields.get("source_sha256") == traffic_source_sha():
+            return fields
+    except (OSError, ValueError):
         pass
     return None
+
+
+def measured_traffic():
+    """HBM bytes per 4096-row call from the committed counter summary, or None."""
+    f = profile_fields("decode_attention_4096rows_hbm_traffic.md")
+    try:
+        return int(f["traffic_bytes_per_call"]) if f else None
+    except (KeyError, ValueError):
+        return None
+
+
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 2.4 GHz, one wave64
+# fp32 VALU instruction per SIMD every 4 cycles (16 lanes per SIMD; no packed
+# fp32 here), in wave-instructions per second.
+VALU_PEAK_GIPS = 256 * 4 * 2.4e9 / 4 / 1e9
+
+
+def alu_line(us_per_call):
+    """VALU instructions per 4096-row call (decode + combine, MFMA excluded),
+    from the committed counter summary, against the vector-issue peak; None
+    when the kernel or plan source has changed since the counters."""
+    f = profile_fields("decode_attention_counters.md")
+    try:
+        valu = int(f["valu_wave_insts_per_call"])
+        mfma = int(f["mfma_insts_per_call"])
+    except (TypeError, KeyError, ValueError):
+        return None
+    achieved = valu / (us_per_call * 1e-6) / 1e9
+    return {"bound": "alu", "achieved": round(achieved, 2), "peak": VALU_PEAK_GIPS, "unit": "G wave-instr/s",
+            "frac": round(achieved / VALU_PEAK_GIPS, 4), "valu_insts_per_call": valu, "mfma_insts_per_call": mfma,
+            "source": "profiles/decode_attention_counters.md (SQ_INSTS_VALU - SQ_INSTS_MFMA)"}
 
 
 def main():
@@ -817,7 +847,8 @@ def main():
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel<128,5,0,1,%d> + combine_kernel<128> (one call; %d splits of %d "
                                "rows)" % (d["plan"]["waves"], d["plan"]["splits"], d["plan"]["split_rows"]),
-                     "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3)},
+                     "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3),
+                     "alu": alu_line(d["us_per_launch"])},
         "device_curve": d["curve"],
         "hbm_stream_ceiling": hbm_stream_ceiling(torch) if args.ceiling else None,
         "calibration_copy_bytes": calib,
