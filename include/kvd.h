@@ -243,8 +243,11 @@ int kvd_attend_merge(const float* partials, int32_t n_part, int32_t n_seq, int32
 typedef struct kvd_ring kvd_ring;
 
 /* Create a ring.  depth >= 0 (0 = ordered path), budget in bytes (the pages'
- * default is 128 MiB per device).  Does no device work.  Returns NULL iff
- * depth < 0 or depth > 64 or host memory runs out (kvd_last_error says which). */
+ * default is 128 MiB per device).  The budget belongs to this ring: one ring
+ * per device is the intended use, and two rings on one device each hold to
+ * their own budget (the device total is their sum).  Does no device work.
+ * Returns NULL iff depth < 0 or depth > 64 or host memory runs out
+ * (kvd_last_error says which). */
 kvd_ring* kvd_ring_create(int32_t depth, size_t budget_bytes);
 
 #define KVD_STAGE_PREFETCH 1
