@@ -191,7 +191,8 @@ struct WaveLds {
     using L_ = Lay<D, VT>;
     static constexpr int K = L_::KT;
     static constexpr int V = L_::VT_;
-    static constexpr int MERGE = G * (D + 2);
+    static constexpr int OFF_O = (2 * G + 3) & ~3;  // o after m [G] and l [G], 16-byte aligned
+    static constexpr int MERGE = OFF_O + G * D;
     static constexpr int DWORDS = (K + V > MERGE ? K + V : MERGE);
 };
 
@@ -480,18 +481,21 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         for (int m = 0; m < KO; ++m) voff[m] = koff[m];
     }
     uint32_t rk[WIDE ? 4 * KW : KN], rv[WIDE ? 4 * VW : VN];
-    auto issue = [&](int r0) {
+    auto issue_k = [&](int r0) {
         const __amdgpu_buffer_rsrc_t kr = sub_rsrc(SG.k, SG.stride, SG.n_rows, CB, g, klead, r0);
-        const __amdgpu_buffer_rsrc_t vr = sub_rsrc(SG.v, SG.vstride, SG.n_rows, CBV, g, vlead, r0);
-        if constexpr (WIDE) {
+        if constexpr (WIDE)
             load_wide<KW>(rk, kr, koff);
-            load_wide<VW>(rv, vr, voff);
-        } else {
+        else
             load_narrow<KN>(rk, kr, koff);
-            load_narrow<VN>(rv, vr, voff);
-        }
     };
-    issue(r_begin + wave * R);
+    auto issue_v = [&](int r0) {
+        const __amdgpu_buffer_rsrc_t vr = sub_rsrc(SG.v, SG.vstride, SG.n_rows, CBV, g, vlead, r0);
+        if constexpr (WIDE)
+            load_wide<VW>(rv, vr, voff);
+        else
+            load_narrow<VN>(rv, vr, voff);
+    };
+    // the query first: its two parts are computed while the first sub-tile is in flight
     float qv[NB][8];
     {
         // q of head n at dims 32 b + 8 gq .. + 7 (zero for the padding columns)
@@ -507,6 +511,8 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             for (int j = 0; j < 8; ++j) qv[b][j] = real ? qv[b][j] : 0.f;
         }
     }
+    issue_k(r_begin + wave * R);
+    issue_v(r_begin + wave * R);
     const int32_t n_vis = A.seq[s].seg[seg].n_vis, seq_splits = A.seq[s].n_split, split_off = A.split_off;
     const float scale_log2e = A.scale_log2e;
     float* const out = A.out;
@@ -542,14 +548,19 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         e = min(max(e, -100), 120);
         rescale = __builtin_ldexpf(1.f, 15 - e);
         unscale = __builtin_ldexpf(1.f, e - 15);
+        // hi = q' rounded toward zero to binary16 (x - hi is then exact in
+        // fp32), lo = the rest rounded the same way: |q' - hi - lo| < 2^-20 |q'|
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float x = qv[b][j] * rescale;
-                const _Float16 hi = (_Float16)x;
-                qh[b][j] = hi;
-                ql[b][j] = (_Float16)(x - (float)hi);
+            for (int j = 0; j < 8; j += 2) {
+                const float x0 = qv[b][j] * rescale, x1 = qv[b][j + 1] * rescale;
+                const auto hi = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+                const auto lo = __builtin_amdgcn_cvt_pkrtz(x0 - (float)hi[0], x1 - (float)hi[1]);
+                qh[b][j] = hi[0];
+                qh[b][j + 1] = hi[1];
+                ql[b][j] = lo[0];
+                ql[b][j + 1] = lo[1];
             }
         }
     }
@@ -584,14 +595,15 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             else
                 __builtin_amdgcn_s_setprio(0);
         }
-        if constexpr (WIDE) {
+        // K is staged before the scores and V only after them, so the scores
+        // start once K has landed and V arrives meanwhile; each register set
+        // takes the next sub-tile's loads as soon as it is copied out.
+        const bool more = t + W < n_sub;
+        if constexpr (WIDE)
             store_wide<KW>(rk, tk, lane);
-            store_wide<VW>(rv, tv, lane);
-        } else {
+        else
             store_narrow<KN>(rk, tk, lane);
-            store_narrow<VN>(rv, tv, lane);
-        }
-        if (t + W < n_sub) issue(row0 + W * R);
+        if (more) issue_k(row0 + W * R);
         wave_lds_sync();
 
 #pragma unroll
@@ -648,6 +660,14 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
                 l += p[j];
             }
             // ---- values
+            if (rs == 0) {
+                if constexpr (WIDE)
+                    store_wide<VW>(rv, tv, lane);
+                else
+                    store_narrow<VN>(rv, tv, lane);
+                if (more) issue_v(row0 + W * R);
+                wave_lds_sync();
+            }
             const uint32_t* const vs = tv + (16 * rs + 4 * gq) * PV + (vlead >> 2);
             const uint8_t* const vc =
                 (const uint8_t*)(tv + (16 * rs + 4 * gq) * PV) + vlead + 2 + (VT ? n : 2 * n);
@@ -711,7 +731,8 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             cs[b] += xchg32(cs[b], lane);
         }
     }
-    float* const mw = (float*)s_lds[wave];  // m [G], l [G], o [G][D]
+    constexpr int OFF = WL::OFF_O;
+    float* const mw = (float*)s_lds[wave];  // m [G], l [G], o [G][D] from OFF
     if (n < G) {
         if (gq == 0) {
             mw[n] = m;
@@ -723,45 +744,52 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             for (int j = 0; j < 4; ++j) {
                 const int i = 4 * gq + j;  // MFMA row of the result
                 if constexpr (VT == 0) {
-                    mw[2 * G + n * D + 32 * b + 2 * i] = o[b][0][j];
-                    mw[2 * G + n * D + 32 * b + 2 * i + 1] = o[b][1][j];
+                    mw[OFF + n * D + 32 * b + 2 * i] = o[b][0][j];
+                    mw[OFF + n * D + 32 * b + 2 * i + 1] = o[b][1][j];
                 } else {
                     // low nibbles and whole bytes -> dims i and i + 16, codes offset by 8
                     const float lo = o[b][0][j], hi = (o[b][1][j] - lo) * 0.0625f;
-                    mw[2 * G + n * D + 32 * b + i] = lo - 8.f * cs[b];
-                    mw[2 * G + n * D + 32 * b + 16 + i] = hi - 8.f * cs[b];
+                    mw[OFF + n * D + 32 * b + i] = lo - 8.f * cs[b];
+                    mw[OFF + n * D + 32 * b + 16 + i] = hi - 8.f * cs[b];
                 }
             }
         }
     }
     __syncthreads();
+    // the W states merged per 4 consecutive dims of a head, in wave order
     const int hq0 = g * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * W) {
-        const int h = idx / D, d = idx - h * D;
+    for (int c = threadIdx.x; c < G * D / 4; c += 64 * W) {
+        const int h = (4 * c) / D, d = 4 * c - h * D;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < W; ++w) M = fmaxf(M, ((const float*)s_lds[w])[h]);
-        float L = 0.f, O = 0.f;
+        float L = 0.f;
+        float4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float* mw2 = (const float*)s_lds[w];
             const float mk = mw2[h];
             const float a = (mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
+            const float4 x = *(const float4*)&mw2[OFF + h * D + d];
             L = fmaf(a, mw2[G + h], L);
-            O = fmaf(a, mw2[2 * G + h * D + d], O);
+            O.x = fmaf(a, x.x, O.x);
+            O.y = fmaf(a, x.y, O.y);
+            O.z = fmaf(a, x.z, O.z);
+            O.w = fmaf(a, x.w, O.w);
         }
         if (single && part_o) {
             const size_t sh = (size_t)s * n_head_q + hq0 + h;
-            part_o[sh * D + d] = O;
+            *(float4*)&part_o[sh * D + d] = O;
             if (d == 0) {
                 part_m[sh] = M;
                 part_l[sh] = L;
             }
         } else if (single) {
-            out[((size_t)s * n_head_q + hq0 + h) * D + d] = O / L;
+            const float4 r = {O.x / L, O.y / L, O.z / L, O.w / L};
+            *(float4*)&out[((size_t)s * n_head_q + hq0 + h) * D + d] = r;
         } else {
             const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
-            po[pi * D + d] = O;
+            *(float4*)&po[pi * D + d] = O;
             if (d == 0) {
                 pm[pi] = M;
                 pl[pi] = L;

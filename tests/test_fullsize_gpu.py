@@ -1,5 +1,5 @@
 """Full-size host-resident stacks in the launch configurations the benchmark
-times, checked against the oracle on sampled outputs:
+times, every output of the checked layers against the oracle:
 - 16384 rows through a depth-1 ring of 128 MiB (whole layers);
 - 131072 rows at 128 MiB, where a whole-layer ring declines and the layer
   is streamed in tiles through the ring;
@@ -74,7 +74,7 @@ def test_128k_tiled_at_128mib(oracle):
     assert a["declined"] == 0 and a["n_acquire_ordered"] == 0 and a["ring_engaged_bytes"] == 134_111_232
     qs = _qs(cfg, cfg.n_layers)
     for l in range(cfg.n_layers):
-        _check_layer(oracle, cfg, host, l, qs[l], res["outs"][l], heads=(0, 7))
+        _check_layer(oracle, cfg, host, l, qs[l], res["outs"][l])
     host.free()
 
 
@@ -101,5 +101,5 @@ def test_128k_whole_layer_ring_at_1gib(oracle):
             assert torch.equal(a, b)
     qs = _qs(cfg, cfg.n_layers)
     for l in range(cfg.n_layers):
-        _check_layer(oracle, cfg, host, l, qs[l], outs[1][l], heads=(3, 6))
+        _check_layer(oracle, cfg, host, l, qs[l], outs[1][l])
     host.free()

@@ -45,22 +45,17 @@ def test_q4_v_matches_oracle(oracle, d, hq, hkv, n):
 
 
 @pytest.mark.parametrize("g_size", [5, 8])
-def test_q4_v_long_context_sampled_heads(oracle, g_size):
+def test_q4_v_long_context_every_head(oracle, g_size):
     """131072 rows x 8 KV heads with q4_0 V (one 12-wave workgroup per CU):
-    sampled KV heads against the oracle run on that head's bytes alone."""
+    the whole output against the oracle."""
     n, hkv, d = 131072, 8, 128
     hq = hkv * g_size
     rng, k, v = _cache(515 + g_size, n, hkv, d)
     q = inputs.random_q(rng, 1, hq, d)
     got = _gpu(q, [[(k, v, 0)]], hkv)
     assert np.isfinite(got).all()
-    kcb, vcb = d // 32 * 34, d // 32 * 18
-    for g in (2, 7):
-        ks = np.ascontiguousarray(k[:, g * kcb:(g + 1) * kcb])
-        vs = np.ascontiguousarray(v[:, g * vcb:(g + 1) * vcb])
-        ref = oracle.attend(q[:, g * g_size:(g + 1) * g_size], [[(ks, vs, 0)]], 1, d, v_type=oracle.V_Q4_0,
-                            threads=8)
-        assert np.abs(got[:, g * g_size:(g + 1) * g_size] - ref).max() <= TOL, g
+    ref = oracle.attend(q, [[(k, v, 0)]], hkv, d, v_type=oracle.V_Q4_0, threads=8)
+    assert np.abs(got - ref).max() <= TOL
 
 
 def test_q4_v_one_row_is_exact(oracle):
