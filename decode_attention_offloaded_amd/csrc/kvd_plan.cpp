@@ -33,9 +33,9 @@ int64_t subtiles_per_cu(const AttendPlan& p, int n_head_kv, int64_t n_cus) {
 // holds three waves per SIMD (its register count); a long context runs best
 // as one workgroup of 12 waves per CU (the split's online-softmax states merge
 // once per CU, and the combine has the fewest partials), a medium one as one
-// of 8, and a short one (a few sub-tiles per CU) as several of 4, whose
-// waves each get more sub-tiles to overlap their loads with.  Measured on
-// MI355X over 4096 ... 131072 rows x 8 KV heads.
+// of 8, and a short one (under 12 sub-tiles per CU) as 4-wave workgroups,
+// whose waves each get more sub-tiles to overlap their loads with.  Measured
+// on MI355X over 2048 ... 131072 rows x 8 KV heads.
 int plan_waves(int64_t subtiles) {
     return subtiles >= kWaves12Subtiles ? 12 : subtiles >= kWaves8Subtiles ? 8 : 4;
 }

@@ -17,7 +17,7 @@ constexpr int kDefaultCUs = 256;          // MI355X compute units, when the devi
 constexpr int64_t kSliceOverheadTiles = 3;  // fixed work of a 4-wave workgroup, in tiles
 constexpr int64_t kBigOverheadTiles = 6;    // fixed work of an 8- or 12-wave workgroup, in tiles
 constexpr int kWavesPerSimd = 3;            // decode-kernel waves resident per SIMD (registers)
-constexpr int64_t kWaves8Subtiles = 24;     // sub-tiles per CU from which 8-wave workgroups are used
+constexpr int64_t kWaves8Subtiles = 12;     // sub-tiles per CU from which 8-wave workgroups are used
 constexpr int64_t kWaves12Subtiles = 96;    // ... and 12-wave ones
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
 

@@ -107,21 +107,21 @@ def _splits(n_rows_list, seg_rows=None):
     return kvd.attend_plan(a)[2]
 
 
-@pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (8192, 64), (12288, 32), (16384, 32),
-                                      (32768, 32), (65536, 32), (131072, 32)])
+@pytest.mark.parametrize("n,splits", [(1024, 16), (2048, 32), (4096, 32), (6144, 32), (8192, 32), (12288, 32),
+                                      (16384, 32), (32768, 32), (65536, 32), (131072, 32)])
 def test_split_plan_single_sequence(n, splits):
     """Splits per KV head on one sequence of n rows x 8 KV heads on 256 CUs
     (the measured fastest, or within 2% of it): 64-row splits up to 2048 rows,
-    128-row ones at 4096 and 8192 rows (4-wave workgroups, one or two per
-    CU), then one 8- or 12-wave workgroup per CU, 32 splits per head."""
+    128-row ones at 4096 rows (4-wave workgroups, one per CU), then one 8- or
+    12-wave workgroup per CU, 32 splits per head."""
     assert _splits([n]) == splits
 
 
-@pytest.mark.parametrize("n,split_rows,waves", [(256, 256, 4), (4096, 128, 4), (8192, 128, 4), (12288, 384, 8),
+@pytest.mark.parametrize("n,split_rows,waves", [(256, 256, 4), (4096, 128, 4), (6144, 192, 8), (8192, 256, 8),
                                                  (16384, 512, 8), (49152, 1536, 12), (131072, 4096, 12)])
 def test_planned_waves(n, split_rows, waves):
     """Rows per split and waves per decode workgroup on 256 CUs, one sequence
-    of n rows x 8 KV heads: 4-wave workgroups below 24 sub-tiles of 16 rows
+    of n rows x 8 KV heads: 4-wave workgroups below 12 sub-tiles of 16 rows
     per CU, 8-wave ones below 96, then 12-wave ones (one per CU)."""
     a, _ = _args()
     a.segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, n, 0, 1088))

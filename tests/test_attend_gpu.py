@@ -300,9 +300,9 @@ def test_graph_replays_match_eager(n, v_type):
 
 def test_workspace_grows_eagerly_and_under_capture():
     """A workspace sized by a short call grows for larger ones: between eager
-    calls (after a device wait: 1024 rows in 16 splits per KV head, then 8192
-    rows in 64) and during graph capture (keeping the old buffer: 8192 rows
-    with 64 query heads, more partials per split).  Outputs equal those of calls with a fresh
+    calls (after a device wait: 1024 rows, then 8192, in 64-row splits) and
+    during graph capture (keeping the old buffer: 8192 rows with 64 query
+    heads, more partials per split).  Outputs equal those of calls with a fresh
     workspace of their own, and the captured call replays to the same bytes."""
     import torch
     from decode_attention_offloaded_amd import kvd
@@ -317,7 +317,7 @@ def test_workspace_grows_eagerly_and_under_capture():
     refs = []
     for q, segs in calls:
         r = torch.empty_like(q)
-        kvd.attend_decode(q, r, segs, 8, workspace=kvd.Workspace())
+        kvd.attend_decode(q, r, segs, 8, workspace=kvd.Workspace(), split_rows=64)
         refs.append(r)
     torch.cuda.synchronize()
     ws = kvd.Workspace()
@@ -326,7 +326,7 @@ def test_workspace_grows_eagerly_and_under_capture():
     with torch.cuda.stream(s):
         for (q, segs), ref in zip(calls[:2], refs[:2]):   # grows between eager calls
             out = torch.empty_like(q)
-            kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s)
+            kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s, split_rows=64)
             s.synchronize()
             assert torch.equal(out, ref)
             sizes.append(ws._buf[torch.cuda.current_device()].numel())
@@ -334,7 +334,7 @@ def test_workspace_grows_eagerly_and_under_capture():
     out = torch.full_like(q, float("nan"))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):                     # grows during capture
-        kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s)
+        kvd.attend_decode(q, out, segs, 8, workspace=ws, stream=s, split_rows=64)
     sizes.append(ws._buf[torch.cuda.current_device()].numel())
     assert sizes[0] < sizes[1] < sizes[2], sizes
     for rep in range(3):
@@ -360,24 +360,24 @@ def test_captured_workspace_survives_eager_growth():
         vd = torch.from_numpy(inputs.random_kv_rows(rng, n, 8, 128)).cuda()
         return torch.from_numpy(inputs.random_q(rng, 1, 40, 128)).cuda(), [[(kd, vd, 0)]]
 
-    small, big = cache(2048), cache(8192)   # 32 and 64 splits per KV head
+    small, big = cache(2048), cache(8192)   # in 64-row splits: 32 and 128 per KV head
     ref = torch.empty_like(small[0])
-    kvd.attend_decode(small[0], ref, small[1], 8, workspace=kvd.Workspace())
+    kvd.attend_decode(small[0], ref, small[1], 8, workspace=kvd.Workspace(), split_rows=64)
     torch.cuda.synchronize()
     ws = kvd.Workspace()
     s = torch.cuda.Stream()
     out = torch.full_like(small[0], float("nan"))
     with torch.cuda.stream(s):
-        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s)   # sizes the workspace
+        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s, split_rows=64)   # sizes the workspace
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s)
+        kvd.attend_decode(small[0], out, small[1], 8, workspace=ws, stream=s, split_rows=64)
     captured = ws._buf[torch.cuda.current_device()]
     cap_ptr, cap_len = captured.data_ptr(), captured.numel()
     del captured
     big_out = torch.empty_like(big[0])
-    kvd.attend_decode(big[0], big_out, big[1], 8, workspace=ws)            # grows the workspace eagerly
+    kvd.attend_decode(big[0], big_out, big[1], 8, workspace=ws, split_rows=64)            # grows the workspace eagerly
     torch.cuda.synchronize()
     assert ws._buf[torch.cuda.current_device()].data_ptr() != cap_ptr
     fillers = [torch.full((cap_len // 4,), 7.0, dtype=torch.float32, device="cuda") for _ in range(4)]
