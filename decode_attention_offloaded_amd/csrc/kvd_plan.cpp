@@ -199,8 +199,22 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus) {
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kTileRows) * kTileRows;
         split_rows = std::max(split_rows, floor_rows);
-        // up to kOneSplitRows visible rows per sequence: one split, no combine launch
-        if (max_vis <= kOneSplitRows) split_rows = std::max<int64_t>(split_rows, ceil_div(max_vis, kTileRows) * kTileRows);
+        // Short contexts: one split per (sequence, segment), no combine launch.
+        // With at most one workgroup per CU, a wave takes the split's
+        // sub-tiles one after another, each waiting on its own loads; one
+        // split beats a split plus the combine launch up to 12 sub-tiles
+        // (192 rows at head_dim 128, 384 at 64), and beyond 128 rows an
+        // 8-wave workgroup keeps each wave at two sub-tiles or fewer.
+        // Measured on MI355X against 64-row splits.
+        const int64_t one_rows = ceil_div(max_vis, kTileRows) * kTileRows;
+        const bool few = slice_workgroups(*p, a->n_head_kv, one_rows) <= n_cus;
+        const int64_t sub_rows = D == 128 ? 16 : 32;  // rows per sub-tile of the decode kernel
+        if (few ? ceil_div(max_vis, sub_rows) <= kOneSplitSubtiles : max_vis <= kOneSplitRows) {
+            split_rows = std::max<int64_t>(split_rows, one_rows);
+            int64_t max_seg = 0;
+            for (const SeqPlan& sp : p->seq) max_seg = std::max<int64_t>({max_seg, sp.seg[0].n_vis, sp.seg[1].n_vis});
+            if (few && max_seg > kOneSplitW8Rows) p->waves = 8;
+        }
         if (split_rows > (1 << 24)) split_rows = 1 << 24;
     }
     p->split_rows = (int32_t)split_rows;

@@ -11,7 +11,9 @@
 namespace kvd {
 
 constexpr int kTileRows = 64;           // rows per tile of the decode kernel (split sizes are multiples)
-constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split
+constexpr int64_t kOneSplitRows = 256;   // contexts this short are not split when workgroups outnumber the CUs
+constexpr int64_t kOneSplitSubtiles = 12;  // ... and, with at most one workgroup per CU, up to this many sub-tiles
+constexpr int64_t kOneSplitW8Rows = 128;   // a sole split longer than this runs as one 8-wave workgroup
 constexpr int kMaxSeqPerLaunch = 16;    // sequences described in one launch's arguments
 constexpr int kDefaultCUs = 256;          // MI355X compute units, when the device cannot be asked
 constexpr int64_t kSliceOverheadTiles = 3;  // fixed work of a 4-wave workgroup, in tiles

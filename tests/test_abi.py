@@ -117,7 +117,7 @@ def test_split_plan_single_sequence(n, splits):
     assert _splits([n]) == splits
 
 
-@pytest.mark.parametrize("n,split_rows,waves", [(256, 256, 4), (4096, 128, 4), (6144, 192, 8), (8192, 256, 8),
+@pytest.mark.parametrize("n,split_rows,waves", [(256, 64, 4), (4096, 128, 4), (6144, 192, 8), (8192, 256, 8),
                                                  (16384, 512, 8), (49152, 1536, 12), (131072, 4096, 12)])
 def test_planned_waves(n, split_rows, waves):
     """Rows per split and waves per decode workgroup on 256 CUs, one sequence
@@ -132,6 +132,31 @@ def test_planned_waves(n, split_rows, waves):
     bad.head_dim = 96
     assert kvd.lib().kvd_attend_plan(ctypes.byref(bad), None, None, None) == kvd.KVD_EINVAL
     assert kvd.lib().kvd_attend_plan(ctypes.byref(a), None, None, None) == kvd.KVD_OK
+
+
+@pytest.mark.parametrize("d,n_head_kv,n,split_rows,waves", [
+    (128, 8, 64, 64, 4), (128, 8, 128, 128, 4), (128, 8, 129, 192, 8), (128, 8, 192, 192, 8), (128, 8, 193, 64, 4),
+    (64, 2, 128, 128, 4), (64, 2, 256, 256, 8), (64, 2, 384, 384, 8), (64, 2, 385, 64, 4), (64, 8, 320, 320, 8)])
+def test_short_context_plan(d, n_head_kv, n, split_rows, waves):
+    """Short contexts with at most one workgroup per CU: one split (no combine
+    launch) up to 12 sub-tiles (16 rows at head_dim 128, 32 at 64), as one
+    8-wave workgroup beyond 128 rows; longer ones are split as usual."""
+    a, _ = _args()
+    a.head_dim = d
+    a.n_head_kv = n_head_kv
+    a.n_head_q = n_head_kv * 4
+    a.segs = (kvd.KvSeg * 1)(kvd.KvSeg(0x10000, 0x20000, n, 0, n_head_kv * d // 32 * 34))
+    sr, w, total = kvd.attend_plan(a)
+    assert (sr, w, total) == (split_rows, waves, -(-n // split_rows))
+
+
+def test_short_context_batch_plan():
+    """Workgroups outnumbering the CUs (64 sequences x 8 KV heads of 250 rows):
+    one split per sequence up to 256 rows, waves from the work per CU."""
+    segs = (kvd.KvSeg * 64)(*[kvd.KvSeg(0x10000, 0x20000, 250, 0, 1088) for _ in range(64)])
+    a, _ = _args(n_seq=64)
+    a.segs = segs
+    assert kvd.attend_plan(a) == (256, 8, 64)
 
 
 def test_split_plan_batch():
