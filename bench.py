@@ -568,8 +568,18 @@ def hbm_stream_ceiling(torch, gib=4, reps=7):
     torch.cuda.empty_cache()
     ms = sorted(times)[len(times) // 2]
     gbs = 2 * n / (ms * 1e-3) / 1e9
-    return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "kernel": "torch.neg, %d GiB float32 read + %d GiB written, median of %d" % (gib, gib, reps)}
+    res = {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+           "kernel": "torch.neg, %d GiB float32 read + %d GiB written, median of %d" % (gib, gib, reps)}
+    # reads only, as the decode kernel's K/V stream does (kvd_hbm_read_probe)
+    rd = kvd_read_ceiling(gib, reps)
+    res["read_only"] = {"GBps": round(rd, 1), "frac_of_peak": round(rd / HBM_PEAK_GBS, 4),
+                        "kernel": "kvd_hbm_read_probe: 16-byte streaming reads of %d GiB, median of %d" % (gib, reps)}
+    return res
+
+
+def kvd_read_ceiling(gib, reps):
+    from decode_attention_offloaded_amd import kvd
+    return kvd.hbm_read_probe(gib << 30, reps)
 
 
 def stream_same_bytes(torch, nbytes, reps=20):

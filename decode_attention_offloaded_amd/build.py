@@ -29,7 +29,7 @@ KERNARG_PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
 # accumulator registers, the softmax rescale of the output accumulators made
 # the compiler copy all of them out and back on every loop iteration.
 MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-HIP_SOURCES = ["kvd_attend.hip"]
+HIP_SOURCES = ["kvd_attend.hip", "kvd_hbm_probe.hip"]
 HOST_SOURCES = ["kvd_plan.cpp", "kvd_errors.cpp", "kvd_ring_core.cpp", "kvd_ring_hip.cpp", "kvd_residency.cpp",
                 "kvd_probe.cpp"]
 

@@ -86,6 +86,8 @@ def _declare(L):
     L.kvd_version.argtypes = []
     L.kvd_link_probe.restype = c_int
     L.kvd_link_probe.argtypes = [c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
+    L.kvd_hbm_read_probe.restype = c_int
+    L.kvd_hbm_read_probe.argtypes = [c_size_t, ctypes.c_int32, ctypes.POINTER(ctypes.c_double)]
     L.kvd_attend_workspace_bytes.restype = c_int
     L.kvd_attend_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(c_size_t)]
     L.kvd_attend_plan.restype = c_int
@@ -151,6 +153,13 @@ def link_probe(nbytes: int, n_streams: int = 2, reps: int = 10) -> float:
     """kvd_link_probe: pinned host-to-device GB/s over n_streams streams (median of reps)."""
     g = ctypes.c_double(0.0)
     _check(lib().kvd_link_probe(int(nbytes), int(n_streams), int(reps), ctypes.byref(g)))
+    return float(g.value)
+
+
+def hbm_read_probe(nbytes: int, reps: int = 7) -> float:
+    """kvd_hbm_read_probe: streaming-read GB/s of device memory (median of reps)."""
+    g = ctypes.c_double(0.0)
+    _check(lib().kvd_hbm_read_probe(int(nbytes), int(reps), ctypes.byref(g)))
     return float(g.value)
 
 

@@ -266,3 +266,11 @@ def test_link_probe_validates_before_touching_the_gpu():
     for args in ((100, 2, 10), (1 << 20, 0, 10), (1 << 20, 5, 10), (1 << 20, 2, 0), ((9 << 30), 1, 1)):
         assert L.kvd_link_probe(args[0], args[1], args[2], ctypes.byref(g)) == kvd.KVD_EINVAL, args
     assert L.kvd_link_probe(1 << 20, 2, 10, None) == kvd.KVD_EINVAL
+
+
+def test_hbm_read_probe_validates_before_touching_the_gpu():
+    L = kvd.lib()
+    g = ctypes.c_double(0.0)
+    for args in ((100, 3), ((1 << 20) + 8, 3), ((1 << 20) - 16, 3), ((65 << 30), 3), (1 << 20, 0), (1 << 20, 1001)):
+        assert L.kvd_hbm_read_probe(args[0], args[1], ctypes.byref(g)) == kvd.KVD_EINVAL, args
+    assert L.kvd_hbm_read_probe(1 << 20, 3, None) == kvd.KVD_EINVAL

@@ -1,6 +1,6 @@
 """Properties of the compiled decode kernels that the tests on the GPU do not
-show: compiles the kernel file to gfx950 assembly (no GPU needed) and reads
-each decode kernel's resource descriptor and code.
+show: compiles the library's HIP sources to gfx950 assembly (no GPU needed)
+and reads each decode kernel's resource descriptor and code.
 
   * no scratch: a register spill would put scratch traffic into the row loop;
   * at most 168 VGPRs, the count at which three waves fit per SIMD: the plan
@@ -24,12 +24,16 @@ def asm(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not installed")
     from decode_attention_offloaded_amd import build as kb
-    out = tmp_path_factory.mktemp("isa") / "kvd_attend.s"
-    cmd = ([HIPCC] + kb.COMMON + ["--offload-arch=" + kb.ARCH] + kb.CODE_OBJECT + kb.NO_PACKED_FP32 +
-           kb.KERNARG_PRELOAD + kb.MFMA_VGPR + ["--cuda-device-only", "-S", "-o", str(out),
-                                               os.path.join(kb.CSRC, "kvd_attend.hip")])
-    subprocess.run(cmd, check=True, capture_output=True)
-    return out.read_text()
+    d = tmp_path_factory.mktemp("isa")
+    text = []
+    for src in kb.HIP_SOURCES:  # every HIP source of the library, with the library's flags
+        out = d / (src + ".s")
+        cmd = ([HIPCC] + kb.COMMON + ["--offload-arch=" + kb.ARCH] + kb.CODE_OBJECT + kb.NO_PACKED_FP32 +
+               kb.KERNARG_PRELOAD + kb.MFMA_VGPR + ["--cuda-device-only", "-S", "-o", str(out),
+                                                   os.path.join(kb.CSRC, src)])
+        subprocess.run(cmd, check=True, capture_output=True)
+        text.append(out.read_text())
+    return "\n".join(text)
 
 
 def _kernels(text):
