@@ -573,7 +573,7 @@ def hbm_stream_ceiling(torch, gib=4, reps=7):
     # reads only, as the decode kernel's K/V stream does (kvd_hbm_read_probe)
     rd = kvd_read_ceiling(gib, reps)
     res["read_only"] = {"GBps": round(rd, 1), "frac_of_peak": round(rd / HBM_PEAK_GBS, 4),
-                        "kernel": "kvd_hbm_read_probe: 16-byte streaming reads of %d GiB, median of %d" % (gib, reps)}
+                        "kernel": "kvd_hbm_read_probe: non-temporal 16-byte streaming reads of %d GiB, median of %d" % (gib, reps)}
     return res
 
 

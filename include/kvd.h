@@ -82,15 +82,15 @@ const char* kvd_version(void);
  * [1, 4], reps outside [1, 1000], NULL gbps) or KVD_EHIP. */
 int kvd_link_probe(size_t bytes, int32_t n_streams, int32_t reps, double* gbps);
 
-/* Device-memory read rate: a streaming-read kernel (16-byte loads, every byte
- * of a `bytes`-byte device buffer read once) timed with HIP events; *gbps =
- * bytes / the median of `reps` launches, after one warm-up launch, in 1e9
- * bytes per second.  Allocates and frees its own buffer (bytes plus a small
- * sink) on the current device and runs on a stream of its own; the call
- * returns when the timed launches are done.  Device-resident decode attention
- * is bound by reading the KV cache ([R4] opening paragraph: the attention
- * every decode token pays for), so its K/V rate is compared with this besides
- * the vendor's peak.
+/* Device-memory read rate: a streaming-read kernel (non-temporal 16-byte
+ * loads, every byte of a `bytes`-byte device buffer read once) timed with HIP
+ * events; *gbps = bytes / the median of `reps` launches, after one warm-up
+ * launch, in 1e9 bytes per second.  Allocates and frees its own buffer (bytes
+ * plus a small sink) on the current device and runs on a stream of its own;
+ * the call returns when the timed launches are done.  Device-resident decode
+ * attention is bound by reading the KV cache ([R4] opening paragraph: the
+ * attention every decode token pays for), so its K/V rate is compared with
+ * this besides the vendor's peak.
  * Returns KVD_OK, KVD_EINVAL (bytes not a multiple of 16 in [1 MiB, 64 GiB],
  * reps outside [1, 1000], NULL gbps; checked before any device work) or
  * KVD_EHIP. */
