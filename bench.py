@@ -582,6 +582,42 @@ def kvd_read_ceiling(gib, reps):
     return kvd.hbm_read_probe(gib << 30, reps)
 
 
+def launch_floor(torch, count=64, reps=20):
+    """The cost of launches alone in a replayed graph, per item: one, and two
+    chained (the second reads what the first wrote, as the combine launch
+    follows the decode launch), torch's elementwise negation of 20 KB (the
+    size of one call's output).  Returns microseconds per item."""
+    xs = [torch.ones(5120, dtype=torch.float32, device="cuda:0") for _ in range(count)]
+    ys = [torch.empty_like(x) for x in xs]
+    zs = [torch.empty_like(x) for x in xs]
+    s = torch.cuda.Stream(device=torch.device("cuda:0"))
+
+    def timed(body):
+        with torch.cuda.stream(s):
+            for i in range(count):
+                body(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                body(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        return round(e0.elapsed_time(e1) * 1e3 / (reps * count), 3)
+
+    one = timed(lambda i: torch.neg(xs[i], out=ys[i]))
+    two = timed(lambda i: (torch.neg(xs[i], out=ys[i]), torch.neg(ys[i], out=zs[i])))
+    return {"one_launch_us": one, "two_chained_launches_us": two,
+            "kernel": "torch.neg of 20 KB, graph-replayed over %d distinct buffers" % count}
+
+
 def stream_same_bytes(torch, nbytes, reps=20):
     """The rate a single streaming launch of one decode call's size reaches
     here: torch's elementwise negation reading nbytes / 2 and writing nbytes / 2,
@@ -870,6 +906,7 @@ def main():
         for n in (4096, 16384, 32768, 131072):
             same[str(n)] = stream_same_bytes(torch, algorithmic_bytes(n, c1.n_head_kv, c1.head_dim, c1.n_head_q))
         out["hbm_stream_ceiling"]["same_bytes_as_call"] = same
+        out["hbm_stream_ceiling"]["launch_floor"] = launch_floor(torch)
     log("streaming ceiling: %s" % out["hbm_stream_ceiling"])
     link = (link_peak(kvd) if (args.pipeline or args.batched or args.tiled or args.residency or args.asym
                                or args.headsplit or args.long or args.devmem) else None)
