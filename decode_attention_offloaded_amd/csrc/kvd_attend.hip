@@ -29,6 +29,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -53,8 +54,9 @@ struct SegDesc {
 
 struct SeqDesc {
     SegDesc seg[2];
-    int32_t split_base;  // first split of this sequence, relative to the launch
+    int32_t split_base;  // first split of this slot's sequence, relative to the launch
     int32_t n_split;     // splits of this sequence
+    int32_t orig;        // the sequence's index among the launch's q / out rows
 };
 
 struct LaunchArgs {
@@ -429,7 +431,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
     if (item >= n_items) return;
     const int lsplit = item / n_head_kv;
     const int g = item - lsplit * n_head_kv;
-    int s = 0, sp = lsplit, seg = 0;
+    int s = 0, so = 0, sp = lsplit, seg = 0;  // slot, its sequence's q / out index, split, segment
     SegDesc SG;
     SG.k = k0;
     SG.v = v0;
@@ -440,6 +442,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
     if (n_seq > 1 || lsplit >= n_split0) {
         // another sequence or the second segment: its descriptor from the block
         while (s + 1 < n_seq && A.seq[s + 1].split_base <= lsplit) ++s;
+        so = A.seq[s].orig;
         sp = lsplit - A.seq[s].split_base;
         const int n0 = A.seq[s].seg[0].n_split;
         if (sp >= n0) {
@@ -453,7 +456,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         SG.vstride = d.vstride;
         SG.row_lo = d.row_lo;
         SG.n_rows = d.n_rows;
-        asm volatile("" ::"s"(SG.k), "s"(SG.v), "s"(SG.stride), "s"(SG.vstride), "s"(SG.row_lo), "s"(SG.n_rows));
+        asm volatile("" ::"s"(SG.k), "s"(SG.v), "s"(SG.stride), "s"(SG.vstride), "s"(SG.row_lo), "s"(SG.n_rows), "s"(so));
     }
     const int r_begin = SG.row_lo + sp * split_rows;
     const int n_head_q = n_head_kv * G;
@@ -511,7 +514,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
     {
         // q of head n at dims 32 b + 8 gq .. + 7 (zero for the padding columns)
         const bool real = n < G;
-        const float* qp = q + ((size_t)s * n_head_q + (size_t)g * G + (real ? n : 0)) * D + 8 * gq;
+        const float* qp = q + ((size_t)so * n_head_q + (size_t)g * G + (real ? n : 0)) * D + 8 * gq;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const float4 a = *(const float4*)(qp + 32 * b);
@@ -789,7 +792,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             O.w = fmaf(a, x.w, O.w);
         }
         if (single && part_o) {
-            const size_t sh = (size_t)s * n_head_q + hq0 + h;
+            const size_t sh = (size_t)so * n_head_q + hq0 + h;
             *(float4*)&part_o[sh * D + d] = O;
             if (d == 0) {
                 part_m[sh] = M;
@@ -797,7 +800,7 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
             }
         } else if (single) {
             const float4 r = {O.x / L, O.y / L, O.z / L, O.w / L};
-            *(float4*)&out[((size_t)s * n_head_q + hq0 + h) * D + d] = r;
+            *(float4*)&out[((size_t)so * n_head_q + hq0 + h) * D + d] = r;
         } else {
             const size_t pi = (size_t)abs_split * n_head_q + hq0 + h;
             *(float4*)&po[pi * D + d] = O;
@@ -871,18 +874,19 @@ __device__ inline void merge_rows(const Load& load, const Hook& after_first_load
 // one-sequence launch start without reading its arguments from memory.
 template <int D>
 __global__ void __launch_bounds__(64)
-combine_kernel(const int32_t n_head_q, const int32_t split_off, const int32_t n_split0, const float* ppm,
-               const float* ppl, const float* ppo, const LaunchArgs A) {
+combine_kernel(const int32_t n_head_q, const int32_t split_off, const int32_t n_split0, const int32_t orig0,
+               const float* ppm, const float* ppl, const float* ppo, const LaunchArgs A) {
     constexpr int NWV = D / 32;
     __shared__ float s_o[64][33];
     const int lane = threadIdx.x;
     const int wave = blockIdx.x % NWV;  // the 32-dim slice of this workgroup
     const int hq = (blockIdx.x / NWV) % n_head_q;
     const int s = blockIdx.x / NWV / n_head_q;
-    int32_t S = n_split0, base = 0;  // sequence 0 starts the launch's splits
+    int32_t S = n_split0, base = 0, so = orig0;  // slot 0 starts the launch's splits
     if (s > 0) {
         S = A.seq[s].n_split;
         base = A.seq[s].split_base;
+        so = A.seq[s].orig;
     }
     if (S <= 1) return;  // written directly by the decode kernel
     const int first = split_off + base;
@@ -898,7 +902,7 @@ combine_kernel(const int32_t n_head_q, const int32_t split_off, const int32_t n_
     auto read_outputs = [&]() { asm volatile("" ::"s"(A.out), "s"(A.part_o), "s"(A.part_m), "s"(A.part_l)); };
     float O, M, L;
     merge_rows(load, read_outputs, S, lane, s_o, O, M, L);
-    if (lane < 32) write_final(A, D, (size_t)s * n_head_q + hq, 32 * wave + lane, O, M, L, wave == 0 && lane == 0);
+    if (lane < 32) write_final(A, D, (size_t)so * n_head_q + hq, 32 * wave + lane, O, M, L, wave == 0 && lane == 0);
 }
 
 // Merge the partial results of n_part calls over disjoint row sets of the
@@ -940,7 +944,7 @@ __global__ void __launch_bounds__(64) spin_kernel(uint32_t ticks) {
 
 typedef void (*decode_fn)(int32_t, int32_t, int32_t, int32_t, const float*, const uint8_t*, const uint8_t*, int32_t,
                           int32_t, int32_t, int32_t, const LaunchArgs);
-typedef void (*combine_fn)(int32_t, int32_t, int32_t, const float*, const float*, const float*, const LaunchArgs);
+typedef void (*combine_fn)(int32_t, int32_t, int32_t, int32_t, const float*, const float*, const float*, const LaunchArgs);
 
 combine_fn pick_combine(int D) { return D == 128 ? combine_kernel<128> : combine_kernel<64>; }
 
@@ -1082,11 +1086,22 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         LaunchArgs L;
         memset(&L, 0, sizeof(L));
         const int64_t base0 = p.seq[s0].split_base;
+        // Slots in order of visible rows, longest first (ties in sequence
+        // order): each XCD then starts its CUs on whole splits and ends on
+        // the short last ones (16 sequences of 1024 ... 10041 rows: 55.1-57.5
+        // -> 52.4-53.6 us per call).  A sequence's arithmetic does not depend
+        // on its slot, so the outputs do not either.
+        int order[kMaxSeqPerLaunch];
+        for (int j = 0; j < ns; ++j) order[j] = j;
+        auto vis = [&](int j) { return (int64_t)p.seq[s0 + j].seg[0].n_vis + p.seq[s0 + j].seg[1].n_vis; };
+        std::stable_sort(order, order + ns, [&](int x, int y) { return vis(x) > vis(y); });
         int64_t nsplit = 0;
         for (int j = 0; j < ns; ++j) {
-            const SeqPlan& sp = p.seq[s0 + j];
-            const kvd_kv_seg* segs = a->segs + (size_t)(s0 + j) * a->n_seg;
+            const int o = order[j];
+            const SeqPlan& sp = p.seq[s0 + o];
+            const kvd_kv_seg* segs = a->segs + (size_t)(s0 + o) * a->n_seg;
             SeqDesc& d = L.seq[j];
+            d.orig = o;
             for (int k = 0; k < 2; ++k) {
                 SegDesc& sd = d.seg[k];
                 const SegPlan& pl = sp.seg[k];
@@ -1101,7 +1116,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                     sd.vstride = (int32_t)(segs[k].v_row_stride ? segs[k].v_row_stride : segs[k].row_stride);
                 }
             }
-            d.split_base = (int32_t)(sp.split_base - base0);
+            d.split_base = (int32_t)nsplit;  // slot order: the splits of slot j follow those of slot j - 1
             d.n_split = sp.n_split;
             nsplit += sp.n_split;
         }
@@ -1136,7 +1151,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         for (int j = 0; j < ns; ++j) multi |= L.seq[j].n_split > 1;
         if (multi) {
             hipLaunchKernelGGL(ck, dim3((unsigned)(ns * n_head_q * (D / 32))), dim3(64), 0, (hipStream_t)stream,
-                               (int32_t)n_head_q, L.split_off, L.seq[0].n_split, L.pm, L.pl, L.po, L);
+                               (int32_t)n_head_q, L.split_off, L.seq[0].n_split, L.seq[0].orig, L.pm, L.pl, L.po, L);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(KVD_EHIP, "combine kernel launch: %s", hipGetErrorString(e));
         }
