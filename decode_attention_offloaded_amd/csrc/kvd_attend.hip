@@ -870,8 +870,9 @@ __device__ inline void merge_rows(const Load& load, const Hook& after_first_load
 // 9.4 -> 8.8 us per call).  A separate launch, so the partials written by the
 // decode kernel are visible without cache maintenance inside a kernel.
 // Leading arguments preloaded into SGPRs as in the decode kernel: the first
-// sequence's split count and the partials, so the partial loads of a
-// one-sequence launch start without reading its arguments from memory.
+// slot's split count and sequence index and the partials, so the partial
+// loads of a one-sequence launch start without reading its arguments from
+// memory.  Slot s merges the sequence the host put there (LaunchArgs.seq[s]).
 template <int D>
 __global__ void __launch_bounds__(64)
 combine_kernel(const int32_t n_head_q, const int32_t split_off, const int32_t n_split0, const int32_t orig0,
