@@ -120,10 +120,10 @@ def device_resident(args, torch, kvd, inputs):
     }
 
 
-def batched_device_point(torch, kvd, inputs, stream, ws, window):
+def batched_device_point(torch, kvd, inputs, stream, ws, window, calls=64):
     """One call over the 16-sequence batch (lognormal lengths, two segments per
     sequence: older and newer halves), every row device-resident: GB/s of the
-    visible K/V rows.  8 distinct layer caches cycled."""
+    visible K/V rows.  A graph of `calls` calls cycling 8 distinct layer caches."""
     from decode_attention_offloaded_amd.batched import cfg4_lengths
     c = inputs.config(4)
     dev = torch.device("cuda:0")
@@ -142,13 +142,14 @@ def batched_device_point(torch, kvd, inputs, stream, ws, window):
         q = torch.from_numpy(inputs.random_q(r, len(lens), c.n_head_q, c.head_dim)).to(dev)
         layers.append((q, segs))
     out = torch.empty_like(layers[0][0])
+    seq = [layers[i % reps] for i in range(max(calls, reps))]
     with torch.cuda.stream(stream):
-        for q, segs in layers:
+        for q, segs in seq:
             kvd.attend_decode(q, out, segs, c.n_head_kv, window=window, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        for q, segs in layers:
+        for q, segs in seq:
             kvd.attend_decode(q, out, segs, c.n_head_kv, window=window, workspace=ws, stream=stream)
     g.replay()
     torch.cuda.synchronize()
@@ -160,7 +161,7 @@ def batched_device_point(torch, kvd, inputs, stream, ws, window):
             g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (nrep * reps)
+    us = e0.elapsed_time(e1) * 1e3 / (nrep * len(seq))
     vis = sum(min(int(n), window) if window else int(n) for n in lens)
     b = 2 * vis * c.row_bytes + 2 * len(lens) * c.n_head_q * c.head_dim * 4
     del layers
@@ -169,8 +170,10 @@ def batched_device_point(torch, kvd, inputs, stream, ws, window):
             "frac_hbm": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def device_curve_point(torch, kvd, inputs, n, stream, ws):
-    """GB/s of one launch over n rows, 8 distinct layers cycled (>= 285 MB apart)."""
+def device_curve_point(torch, kvd, inputs, n, stream, ws, calls=64):
+    """GB/s of one call over n rows: a graph of `calls` calls (one decode step
+    of 64 layers, as the headline measures it) cycling at least 2 and at most
+    16 distinct layer caches, >= 2.5 GB between a layer's reuses."""
     c = inputs.config(1)
     dev = torch.device("cuda:0")
     reps = max(2, min(16, int(2.5e9 // (2 * n * c.row_bytes))))
@@ -183,13 +186,14 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
     qs = [torch.from_numpy(inputs.random_q(np.random.default_rng([n, i]), 1, c.n_head_q, c.head_dim)).to(dev)
           for i in range(reps)]
     out = torch.empty_like(qs[0])
+    idx = [i % reps for i in range(max(calls, reps))]
     with torch.cuda.stream(stream):
-        for i in range(reps):
+        for i in idx:
             kvd.attend_decode(qs[i], out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        for i in range(reps):
+        for i in idx:
             kvd.attend_decode(qs[i], out, [[(ks[i], vs[i], 0)]], c.n_head_kv, workspace=ws, stream=stream)
     g.replay()
     torch.cuda.synchronize()
@@ -201,7 +205,7 @@ def device_curve_point(torch, kvd, inputs, n, stream, ws):
             g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (nrep * reps)
+    us = e0.elapsed_time(e1) * 1e3 / (nrep * len(idx))
     b = algorithmic_bytes(n, c.n_head_kv, c.head_dim, c.n_head_q)
     del ks, vs
     torch.cuda.empty_cache()
@@ -618,25 +622,27 @@ def launch_floor(torch, count=64, reps=20):
             "kernel": "torch.neg of 20 KB, graph-replayed over %d distinct buffers" % count}
 
 
-def stream_same_bytes(torch, nbytes, reps=20):
+def stream_same_bytes(torch, nbytes, reps=20, calls=64):
     """The rate a single streaming launch of one decode call's size reaches
     here: torch's elementwise negation reading nbytes / 2 and writing nbytes / 2,
-    graph-replayed over distinct buffers (at least 2.5 GB in all, as the decode
-    calls cycle distinct layers), so launch and first-byte latency weigh as
-    they do for a call.  Returns {"bytes", "us", "GBps", "frac_of_peak"}."""
+    a graph of `calls` launches (as the decode calls are measured) cycling
+    distinct buffers (at least 2.5 GB in all, as the decode calls cycle
+    distinct layers), so launch and first-byte latency weigh as they do for a
+    call.  Returns {"bytes", "us", "GBps", "frac_of_peak"}."""
     n = nbytes // 8
     count = max(4, min(64, int(2.5e9 // nbytes)))
     xs = [torch.ones(n, dtype=torch.float32, device="cuda:0") for _ in range(count)]
     ys = [torch.empty_like(x) for x in xs]
     s = torch.cuda.Stream(device=torch.device("cuda:0"))
+    idx = [i % count for i in range(max(calls, count))]
     with torch.cuda.stream(s):
-        for x, y in zip(xs, ys):
-            torch.neg(x, out=y)
+        for i in idx:
+            torch.neg(xs[i], out=ys[i])
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        for x, y in zip(xs, ys):
-            torch.neg(x, out=y)
+        for i in idx:
+            torch.neg(xs[i], out=ys[i])
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -646,7 +652,7 @@ def stream_same_bytes(torch, nbytes, reps=20):
             g.replay()
         e1.record(s)
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (reps * count)
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(idx))
     del xs, ys, g
     torch.cuda.empty_cache()
     moved = 8 * n
