@@ -178,6 +178,28 @@ def test_deterministic_and_pointer_independent():
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
+def test_sequence_order_does_not_change_any_output(oracle):
+    """A launch fills its slots longest sequence first and each slot carries
+    its sequence's query/output index: the same 16 sequences (two segments
+    each, lengths 300 ... 9000 rows) given in reverse order give every
+    sequence's output bit for bit, and the output matches the oracle."""
+    hq, hkv, d = 40, 8, 128
+    rng = np.random.default_rng(1616)
+    lens = [300, 9000, 1200, 4100, 700, 6400, 2500, 8000, 1024, 3333, 5000, 450, 7777, 2048, 6100, 999]
+    segs = []
+    for n in lens:
+        k = inputs.random_kv_rows(rng, n, hkv, d)
+        v = inputs.random_kv_rows(rng, n, hkv, d)
+        h = n // 2
+        segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
+    q = inputs.random_q(rng, len(lens), hq, d)
+    fwd = gpu_attend(q, segs, hkv)
+    rev = gpu_attend(q[::-1].copy(), segs[::-1], hkv)
+    assert np.array_equal(fwd, rev[::-1])
+    ref = oracle.attend(q, segs, hkv, d, threads=8)
+    check(fwd, ref)
+
+
 def test_long_context_every_head(oracle):
     """131072 rows x 40/8 heads (the long-context layer, one 12-wave
     workgroup per CU, 32 splits per KV head): the whole output against the
