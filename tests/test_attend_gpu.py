@@ -46,7 +46,7 @@ def test_config1_full(oracle):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (10, 2), (40, 8), (16, 2), (32, 32), (64, 16)])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (10, 2), (40, 8), (16, 2), (32, 32), (64, 16), (8, 1), (5, 1)])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 160, 200, 384, 777])
 def test_shapes_and_ragged_tails(oracle, d, hq, hkv, n):
     rng, k, v = make_cache(1000 + n + d + hq, n, hkv, d)
