@@ -114,9 +114,11 @@ int kvd_hbm_read_probe(size_t bytes, int32_t reps, double* gbps);
  * Work is split over (sequence, KV head, row range); each split keeps an
  * online-softmax partial and the partials of one (sequence, query head) are
  * merged in a fixed order by a second launch on the same stream.  The split
- * plan depends only on the shapes (never on pointers, timing or the ring), so
- * two calls with equal shapes and equal input bytes give bit-identical
- * outputs.
+ * plan depends only on the shapes and the device's compute-unit count (never
+ * on pointers, timing or the ring), so two calls with equal shapes and equal
+ * input bytes give bit-identical outputs.  The order in which sequences are
+ * given changes no sequence's output either (the launch deals them out longest
+ * first).
  */
 typedef struct kvd_kv_seg {
     const void* k;       /* device: K row 0 of this segment (q8_0 rows) */
