@@ -40,6 +40,18 @@ int plan_waves(int64_t subtiles) {
     return subtiles >= kWaves12Subtiles ? 12 : subtiles >= kWaves8Subtiles ? 8 : 4;
 }
 
+// Share of the chip's time that splits of `rows` rows in 8- or 12-wave
+// workgroups (one per CU at a time) fill with rows: visible rows x KV heads
+// over CUs x split rows x rounds of workgroups.  Equal sequences fill nearly
+// all of it; sequences of unequal length leave the CUs of their short last
+// splits idle.
+double big_plan_fill(const AttendPlan& p, int n_head_kv, int64_t rows, int64_t n_cus) {
+    int64_t vis = 0;
+    for (const SeqPlan& sp : p.seq) vis += (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis;
+    const int64_t rounds = ceil_div(slice_workgroups(p, n_head_kv, rows), n_cus);
+    return (double)(vis * n_head_kv) / ((double)n_cus * (double)rows * (double)rounds);
+}
+
 // Relative time per unit of work of a 4-wave workgroup when the busiest CU
 // runs `per_cu` of them: one per CU (one wave per SIMD) hides little latency;
 // up to kWavesPerSimd are resident at once, beyond that they queue in rounds.
@@ -192,10 +204,32 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus) {
     int64_t max_vis = 0;
     for (const SeqPlan& sp : p->seq) max_vis = std::max<int64_t>(max_vis, (int64_t)sp.seg[0].n_vis + sp.seg[1].n_vis);
     p->n_cus = n_cus;
-    p->waves = plan_waves(subtiles_per_cu(*p, a->n_head_kv, n_cus));
+    // A call runs as consecutive launches of up to kMaxSeqPerLaunch sequences,
+    // and each launch should fill the chip: the work per CU, the wave count
+    // and the split size are weighed against the CUs of all the launches
+    // (64 sequences of 4096 rows x 8 KV heads: one 4096-row split per
+    // sequence gave each launch 128 workgroups, half the chip, 204 us per
+    // call; 2048-row splits fill it, 155 us).
+    const int64_t plan_cus = (int64_t)n_cus * ceil_div(a->n_seq, kMaxSeqPerLaunch);
+    p->waves = plan_waves(subtiles_per_cu(*p, a->n_head_kv, plan_cus));
     int64_t split_rows = a->split_rows;
     if (split_rows == 0) {
-        split_rows = (int64_t)kTileRows * tiles_per_split(*p, a->n_head_kv, max_vis, n_cus, p->waves);
+        int64_t k = tiles_per_split(*p, a->n_head_kv, max_vis, plan_cus, p->waves);
+        // Sequences of unequal length: where 8- or 12-wave workgroups would
+        // leave more than kBigPlanMinFill of the chip's time idle, 4-wave
+        // workgroups in their own (smaller) splits, up to three per CU, share
+        // the CUs out more evenly.  Measured on MI355X, 16 sequences of
+        // lognormal lengths (1024 ... 10041 rows) in two segments: 54.2 ->
+        // 49.8 us per call, with a 4096-row window 41.6 -> 34.2 us; 16 of
+        // 256 ... 8192 rows: 31.5 -> 27.8 us.  Single sequences and equal
+        // ones fill the chip and keep their plan (4-wave workgroups there
+        // lose 2-25%).
+        if (p->waves != 4 && a->n_seq > 1 &&
+            big_plan_fill(*p, a->n_head_kv, k * kTileRows, plan_cus) < kBigPlanMinFill) {
+            p->waves = 4;
+            k = tiles_per_split(*p, a->n_head_kv, max_vis, plan_cus, p->waves);
+        }
+        split_rows = (int64_t)kTileRows * k;
         // segments split separately: allow one extra split per segment
         const int64_t floor_rows = ceil_div(ceil_div(max_vis, kMaxSplits - 2), kTileRows) * kTileRows;
         split_rows = std::max(split_rows, floor_rows);
@@ -213,7 +247,7 @@ int plan_attend(const kvd_attn_args* a, AttendPlan* p, int n_cus) {
             split_rows = std::max<int64_t>(split_rows, one_rows);
             int64_t max_seg = 0;
             for (const SeqPlan& sp : p->seq) max_seg = std::max<int64_t>({max_seg, sp.seg[0].n_vis, sp.seg[1].n_vis});
-            if (few && max_seg > kOneSplitW8Rows) p->waves = 8;
+            p->waves = few && max_seg > kOneSplitW8Rows ? 8 : plan_waves(subtiles_per_cu(*p, a->n_head_kv, n_cus));
         }
         if (split_rows > (1 << 24)) split_rows = 1 << 24;
     }

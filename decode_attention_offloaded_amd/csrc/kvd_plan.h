@@ -21,6 +21,7 @@ constexpr int64_t kBigOverheadTiles = 6;    // fixed work of an 8- or 12-wave wo
 constexpr int kWavesPerSimd = 3;            // decode-kernel waves resident per SIMD (registers)
 constexpr int64_t kWaves8Subtiles = 12;     // sub-tiles per CU from which 8-wave workgroups are used
 constexpr int64_t kWaves12Subtiles = 96;    // ... and 12-wave ones
+constexpr double kBigPlanMinFill = 0.85;     // 8/12-wave plans filling less of the chip go to 4 waves
 constexpr int kMaxSplits = 256;         // splits per (sequence, KV head) merged by one workgroup
 
 struct SegPlan {

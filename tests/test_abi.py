@@ -159,11 +159,49 @@ def test_short_context_batch_plan():
     assert kvd.attend_plan(a) == (256, 8, 64)
 
 
+def _plan_of(seg_lists):
+    """kvd_attend_plan for sequences given as lists of (n_rows, pos0), 40 query / 8 KV heads."""
+    segs = [kvd.KvSeg(0x10000, 0x20000, n, p0, 1088) for sl in seg_lists for n, p0 in sl]
+    a, _ = _args(n_seq=len(seg_lists), n_seg=len(seg_lists[0]))
+    a.segs = (kvd.KvSeg * len(segs))(*segs)
+    return kvd.attend_plan(a)
+
+
 def test_split_plan_batch():
-    """16 sequences in two segments each (84227 rows in all, so 12-wave
-    workgroups): 1664-row splits, 64 in all, two workgroups per CU."""
+    """16 sequences of unequal length in two segments each (80231 rows): 12-wave
+    workgroups in 1664-row splits would fill 75% of the chip's time (two
+    rounds, many short last splits), so the plan takes 4-wave workgroups in
+    1024-row splits, 92 in all, about three per CU."""
     lens = [1024, 1024, 1862, 1990, 2813, 3712, 3769, 4264, 5376, 5801, 6363, 6588, 7292, 8678, 9634, 10041]
-    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 1664) + -(-(n - n // 2) // 1664) for n in lens) == 64
+    assert _splits(lens, seg_rows=True) == sum(-(-(n // 2) // 1024) + -(-(n - n // 2) // 1024) for n in lens) == 92
+    assert _plan_of([[(n // 2, 0), (n - n // 2, n // 2)] for n in lens]) == (1024, 4, 92)
+
+
+@pytest.mark.parametrize("seg_lists,plan", [
+    ([[(4096, 0)]] * 16, (2048, 12, 32)),                              # equal: fills the chip
+    ([[(16383, 0), (1, 16383)]] * 4, (2368, 12, 32)),                 # equal, each with a one-row tail
+    ([[(131072, 0)], [(65536, 0)]], (6272, 12, 32)),                  # unequal but long: 98% filled
+    ([[(8192, 0)]] * 8 + [[(2048, 0)]] * 8, (2752, 12, 32)),          # two lengths: 93% filled
+    ([[(n, 0)] for n in (256, 322, 406, 512, 645, 812, 1024, 1290, 1625, 2048, 2580, 3250, 4096, 5160, 6501, 8192)],
+     (448, 4, 94)),                                                    # 256 ... 8192 rows: 73% -> 4 waves
+])
+def test_plan_fill_rule(seg_lists, plan):
+    """8- and 12-wave workgroups are kept where their splits fill at least 85%
+    of the chip's time (visible rows x KV heads over CUs x split rows x
+    rounds); below that, sequences of unequal length go to 4-wave workgroups
+    in their own splits.  Single sequences always keep the 8/12-wave plan."""
+    assert _plan_of(seg_lists) == plan
+
+
+@pytest.mark.parametrize("n_seq,n,plan", [(16, 4096, (2048, 12, 32)), (17, 4096, (384, 4, 187)),
+                                          (32, 4096, (2048, 12, 64)), (64, 4096, (2048, 12, 128)),
+                                          (64, 1024, (512, 8, 128))])
+def test_plan_per_launch_capacity(n_seq, n, plan):
+    """A call of more than 16 sequences runs as consecutive launches of up to
+    16, so splits and waves are chosen for the CUs of all its launches: each
+    launch of 16 sequences of 4096 rows gets 2048-row splits (256 workgroups),
+    not one 4096-row split (128, half the chip)."""
+    assert _plan_of([[(n, 0)]] * n_seq) == plan
 
 
 def test_workspace_too_small_is_rejected():
