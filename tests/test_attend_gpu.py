@@ -454,3 +454,44 @@ def test_more_sequences_than_one_launch(oracle, v_type):
     assert np.abs(got - ref).max() <= 1e-3
     if not one_row:
         assert np.abs(merged.cpu().numpy() - ref).max() <= 1e-3
+
+
+def _plan_of(q, segs_np, n_head_kv):
+    """(split rows, waves, total splits) that a call with these shapes gets."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    qd = to_dev(q)
+    segs = [[(to_dev(k[:1]), to_dev(v[:1]), p0) for (k, v, p0) in seq] for seq in segs_np]
+    a, keep = kvd.make_args(qd, torch.empty_like(qd), segs, n_head_kv)
+    for i, seq in enumerate(segs_np):  # the real row counts (the plan reads shapes only)
+        for j, (k, _, _) in enumerate(seq):
+            a.segs[i * len(seq) + j].n_rows = k.shape[0]
+    return kvd.attend_plan(a)
+
+
+@pytest.mark.parametrize("case", ["unequal_to_4_waves", "unequal_tails_to_4_waves", "seventeen_per_launch"])
+def test_planner_paths(oracle, case):
+    """Each plan path on the GPU against the oracle, with the plan checked
+    first: 16 sequences of 256 ... 8192 rows (8-wave splits would fill 73% of
+    the chip, so 4-wave workgroups in 448-row splits); the same with a one-row
+    tail segment per sequence (576-row splits); 17 sequences of 4096 rows (two
+    launches, splits sized for both)."""
+    hq, hkv, d = 40, 8, 128
+    rng = np.random.default_rng({"unequal_to_4_waves": 81, "unequal_tails_to_4_waves": 82, "seventeen_per_launch": 83}[case])
+    if case == "seventeen_per_launch":
+        lens, want = [4096] * 17, (384, 4, 187)
+    else:
+        lens = [int(n) for n in np.geomspace(256, 8192, 16)]
+        want = (448, 4, 94) if case == "unequal_to_4_waves" else (576, 4, 91)
+    segs = []
+    for n in lens:
+        k = inputs.random_kv_rows(rng, n, hkv, d)
+        v = inputs.random_kv_rows(rng, n, hkv, d)
+        if case == "unequal_tails_to_4_waves":
+            segs.append([(k[:n - 1], v[:n - 1], 0), (k[n - 1:], v[n - 1:], n - 1)])
+        else:
+            segs.append([(k, v, 0)])
+    q = inputs.random_q(rng, len(lens), hq, d)
+    assert _plan_of(q, segs, hkv) == want
+    ref = oracle.attend(q, segs, hkv, d, threads=8)
+    check(gpu_attend(q, segs, hkv), ref)
