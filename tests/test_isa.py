@@ -53,14 +53,23 @@ def _field(desc, key):
 
 
 def test_every_variant_is_built(asm):
-    # head_dim 64/128 x group 1..8 x q8_0/q4_0 V x wide/narrow loads x 4/8/12 waves
-    assert len(_kernels(asm)) == 2 * 8 * 2 * 2 * 3
+    # head_dim 64/128 x group 1..8 x q8_0/q4_0 V x the load modes each wave
+    # count is launched with: 4 waves dword / 16-byte via registers / 16-byte
+    # into LDS, 8 waves dword / into LDS, 12 waves dword / via registers
+    names = _kernels(asm)
+    assert len(names) == 2 * 8 * 2 * (3 + 2 + 2)
+    modes = {(int(w), int(m)) for m, w in (re.search(r"decode_kernelILi\d+ELi\dELi\dELi(\d)ELi(\d+)E", n).groups()
+                                           for n in names)}
+    assert modes == {(4, 0), (4, 1), (4, 2), (8, 0), (8, 2), (12, 0), (12, 1)}
 
 
-def test_no_scratch_and_three_waves_per_simd(asm):
+def test_no_scratch_and_waves_per_simd(asm):
+    """No spills; 4- and 12-wave kernels fit three waves per SIMD (up to three
+    4-wave workgroups, or one 12-wave one, per CU), 8-wave kernels two."""
     for name, (desc, _) in _kernels(asm).items():
         assert _field(desc, "amdhsa_private_segment_fixed_size") == 0, name
-        assert _field(desc, "amdhsa_next_free_vgpr") <= 168, name
+        w = int(re.search(r"decode_kernelILi\d+ELi\dELi\dELi\dELi(\d+)E", name).group(1))
+        assert _field(desc, "amdhsa_next_free_vgpr") <= (256 if w == 8 else 168), name
 
 
 def test_mfma_in_every_decode_kernel_and_no_packed_fp32(asm):
