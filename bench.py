@@ -787,6 +787,13 @@ def traffic_source_sha():
     return h.hexdigest()
 
 
+def load_mode(waves, workgroups, n_cus):
+    """The decode kernel's load mode (its WIDE argument) for a launch of
+    16-byte-aligned K/V, by the launch's rule: 2 (straight into LDS) where a
+    CU runs at most 8 waves, else 1 (staged in registers)."""
+    return 2 if waves == 8 or (waves == 4 and workgroups <= 2 * n_cus) else 1
+
+
 def profile_fields(name):
     """The machine-readable fields (indented `key: value` lines) of a committed
     profile summary, or None when the kernel or plan source has changed since
@@ -897,8 +904,10 @@ def main():
                    "layers_per_step": d["layers_per_step"], "kv": "q8_0 (34-byte blocks)"},
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "decode_kernel<128,5,0,1,%d> + combine_kernel<128> (one call; %d splits of %d "
-                               "rows)" % (d["plan"]["waves"], d["plan"]["splits"], d["plan"]["split_rows"]),
+                     "kernel": "decode_kernel<128,5,0,%d,%d> + combine_kernel<128> (one call; %d splits of %d "
+                               "rows)" % (load_mode(d["plan"]["waves"], 8 * d["plan"]["splits"],
+                                                    torch.cuda.get_device_properties(0).multi_processor_count),
+                                          d["plan"]["waves"], d["plan"]["splits"], d["plan"]["split_rows"]),
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3),
                      "alu": alu_line(d["us_per_launch"])},
         "device_curve": d["curve"],
