@@ -495,3 +495,39 @@ def test_planner_paths(oracle, case):
     assert _plan_of(q, segs, hkv) == want
     ref = oracle.attend(q, segs, hkv, d, threads=8)
     check(gpu_attend(q, segs, hkv), ref)
+
+
+@pytest.mark.parametrize("case", ["4096_lds", "16384_lds", "65536_registers", "batch_registers", "batch_lds", "q4_0_lds"])
+def test_load_modes_are_bit_identical(oracle, case):
+    """The same call with 16-byte-aligned rows (16-byte loads: straight into
+    LDS, or staged in registers at 12 waves per CU) and with rows padded to a
+    stride that is not a multiple of 16 (dword loads) gets the same plan, the
+    same LDS contents and so bit-identical outputs; both match the oracle."""
+    import torch
+    from decode_attention_offloaded_amd import kvd
+    hq, hkv, d = 40, 8, 128
+    rng = np.random.default_rng(sum(map(ord, case)))
+    lens = {"4096_lds": [4096], "16384_lds": [16384], "65536_registers": [65536], "q4_0_lds": [4096],
+            "batch_registers": [int(n) for n in np.geomspace(256, 8192, 16)], "batch_lds": [2048] * 16}[case]
+    v_type = 1 if case == "q4_0_lds" else 0
+    vgen = inputs.random_kv_rows_q4_0 if v_type else inputs.random_kv_rows
+    segs_np = [[(inputs.random_kv_rows(rng, n, hkv, d), vgen(rng, n, hkv, d), 0)] for n in lens]
+    q = inputs.random_q(rng, len(lens), hq, d)
+
+    def run(pad):
+        qd = to_dev(q)
+        out = torch.full_like(qd, float("nan"))
+        segs = []
+        for ((k, v, p0),) in segs_np:
+            if pad:
+                k = np.concatenate([k, np.full((k.shape[0], pad), 0x5A, np.uint8)], axis=1)
+                v = np.concatenate([v, np.full((v.shape[0], pad), 0xA5, np.uint8)], axis=1)
+            segs.append([(to_dev(k), to_dev(v), p0)])
+        kvd.attend_decode(qd, out, segs, hkv, v_type=v_type)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    aligned, padded = run(0), run(8)
+    assert np.array_equal(aligned, padded), np.max(np.abs(aligned - padded))
+    ref = oracle.attend(q, segs_np, hkv, d, threads=8, v_type=oracle.V_Q4_0 if v_type else oracle.V_Q8_0)
+    check(aligned, ref)
