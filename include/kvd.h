@@ -177,8 +177,11 @@ int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
 /* The launch plan a call with these arguments gets on the current device,
  * without launching anything (validates the arguments too): rows per split,
  * waves per decode workgroup (4, 8 or 12, chosen from the work per compute
- * unit) and the splits of all sequences together.  Any output pointer may be
- * NULL.  Returns KVD_OK or KVD_EINVAL.  The plan depends on the shapes and the
+ * unit; calls of several sequences whose 8- or 12-wave splits would fill
+ * under 85% of the chip's time take 4) and the splits of all sequences
+ * together.  A call of more than 16 sequences runs as consecutive launches of
+ * up to 16, all with these split rows and waves, sized for the compute units
+ * of all its launches.  Any output pointer may be NULL.  Returns KVD_OK or KVD_EINVAL.  The plan depends on the shapes and the
  * device's compute-unit count only ("F5 -- Advanced KV Cache Techniques", M4:
  * split-K decode over row ranges, merged by running maxima and sums). */
 int kvd_attend_plan(const kvd_attn_args* args, int32_t* split_rows, int32_t* waves, int64_t* total_splits);
