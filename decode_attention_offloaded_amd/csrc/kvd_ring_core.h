@@ -124,7 +124,6 @@ private:
     StreamH xfer_[kXferStreams] = {nullptr, nullptr};
     std::vector<Slot> slots_;
     uint64_t cursor_ = 0;        // deliveries issued so far
-    uint64_t last_xfer_ = 0;     // cursor+1 of the delivery last put on the transfer stream (0 = none)
     kvd_ring_stats st_{};
     uint32_t delay_max_us_ = 0;
     uint64_t delay_state_ = 1;
