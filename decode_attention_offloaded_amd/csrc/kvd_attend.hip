@@ -1229,8 +1229,8 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         L.scale_log2e = scale_log2e;
         // 16-byte loads go straight into LDS where a CU runs at most 8 waves
         // (8-wave workgroups, or 4-wave ones at most two per CU): 4096 rows
-        // 8.42 -> 8.20 us per call, 16384 rows 13.9 -> 13.5, 32768 rows
-        // 21.3 -> 20.0.  With 12 waves per CU, register staging is faster
+        // 8.45 -> 8.25 us per call, 16384 rows 14.1 -> 13.5, 32768 rows
+        // 21.3 -> 20.2.  With 12 waves per CU, register staging is faster
         // (131072 rows 58.5 against 59.9 us; the 16-sequence batch's three
         // 4-wave workgroups per CU 48.7 against 50.6).
         const int mode = !wide ? 0
