@@ -529,13 +529,15 @@ decode_kernel(const int32_t n_items, const int32_t kv_seq, const int32_t split_r
         for (int m = 0; m < KO; ++m) voff[m] = koff[m];
     }
     uint32_t rk[WIDE ? 4 * KW : KN], rv[WIDE ? 4 * VW : VN];
-    // 4-wave workgroups (small calls) stream K/V non-temporally, which leaves
-    // the small data a call reuses (query, split partials) in the caches:
-    // 8.70 -> 8.53 us per 4096-row call.  The larger plans keep the default
-    // policy: there a line that straddles two KV heads is read by two
-    // workgroups of one XCD, and non-temporal loads made the second one miss
-    // (131072 rows: 58.2 -> 63.2 us).
-    constexpr int AUX = W == 4 ? kLoadNonTemporal : 0;
+    // 4-wave workgroups of small calls (at most two per CU: loads straight
+    // into LDS, or dword loads) stream K/V non-temporally, which leaves the
+    // small data a call reuses (query, split partials) in the caches: 8.70 ->
+    // 8.53 us per 4096-row call.  The other plans keep the default policy:
+    // there a line that straddles two KV heads is read by two workgroups of
+    // one XCD, and non-temporal loads made the second one miss (131072 rows:
+    // 58.2 -> 63.2 us; 16 sequences of 1024 ... 10041 rows, three 4-wave
+    // workgroups per CU with register staging: 47.6 -> 48.6 us).
+    constexpr int AUX = (W == 4 && WIDE != 1) ? kLoadNonTemporal : 0;
     auto lds_k = [&](int r0, uint32_t* t) {  // WIDE == 2
         const __amdgpu_buffer_rsrc_t kr = sub_rsrc(SG.k, SG.stride, SG.n_rows, CB, g, klead, r0);
 #pragma unroll
