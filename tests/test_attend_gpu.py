@@ -531,3 +531,23 @@ def test_load_modes_are_bit_identical(oracle, case):
     assert np.array_equal(aligned, padded), np.max(np.abs(aligned - padded))
     ref = oracle.attend(q, segs_np, hkv, d, threads=8, v_type=oracle.V_Q4_0 if v_type else oracle.V_Q8_0)
     check(aligned, ref)
+
+
+@pytest.mark.parametrize("window", [0, 700])
+def test_seventeen_sequences_in_two_segments(oracle, window):
+    """17 sequences of unequal length, each in two segments: two launches (16
+    sequences, then one whose second segment the kernel finds through its
+    descriptor), plans sized for both launches, with and without a window;
+    every output against the oracle."""
+    hq, hkv, d = 40, 8, 128
+    rng = np.random.default_rng(1700 + window)
+    lens = [int(n) for n in rng.integers(300, 3000, size=17)]
+    segs = []
+    for n in lens:
+        k = inputs.random_kv_rows(rng, n, hkv, d)
+        v = inputs.random_kv_rows(rng, n, hkv, d)
+        h = n // 3
+        segs.append([(k[:h], v[:h], 0), (k[h:], v[h:], h)])
+    q = inputs.random_q(rng, len(lens), hq, d)
+    ref = oracle.attend(q, segs, hkv, d, window=window, threads=8)
+    check(gpu_attend(q, segs, hkv, window=window), ref)
