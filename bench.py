@@ -95,6 +95,7 @@ def device_resident(args, torch, kvd, inputs):
     ms_step = ms / args.steps
     plan_args, _keep = kvd.make_args(qs[0], outs[0], [[(ks[0], vs[0], 0)]], c.n_head_kv)
     split_rows, waves, n_splits = kvd.attend_plan(plan_args)
+    load_mode = kvd.attend_load_mode(plan_args)
     launches = args.steps * L
     us_launch = ms * 1e3 / launches
     per_launch = algorithmic_bytes(c.n_ctx, c.n_head_kv, c.head_dim, c.n_head_q)
@@ -115,7 +116,7 @@ def device_resident(args, torch, kvd, inputs):
     return {
         "ms_per_step": ms_step, "value": gbs, "us_per_launch": us_launch, "bytes_per_launch": per_launch,
         "layers_per_step": L, "curve": curve,
-        "plan": {"split_rows": split_rows, "waves": waves, "splits": n_splits},
+        "plan": {"split_rows": split_rows, "waves": waves, "splits": n_splits, "load_mode": load_mode},
         "ws": ws, "q": qs[0], "k": ks[0], "v": vs[0],
     }
 
@@ -787,13 +788,6 @@ def traffic_source_sha():
     return h.hexdigest()
 
 
-def load_mode(waves, workgroups, n_cus):
-    """The decode kernel's load mode (its WIDE argument) for a launch of
-    16-byte-aligned K/V, by the launch's rule: 2 (straight into LDS) where a
-    CU runs at most 8 waves, else 1 (staged in registers)."""
-    return 2 if waves == 8 or (waves == 4 and workgroups <= 2 * n_cus) else 1
-
-
 def profile_fields(name):
     """The machine-readable fields (indented `key: value` lines) of a committed
     profile summary, or None when the kernel or plan source has changed since
@@ -905,9 +899,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(d["value"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(d["value"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel<128,5,0,%d,%d> + combine_kernel<128> (one call; %d splits of %d "
-                               "rows)" % (load_mode(d["plan"]["waves"], 8 * d["plan"]["splits"],
-                                                    torch.cuda.get_device_properties(0).multi_processor_count),
-                                          d["plan"]["waves"], d["plan"]["splits"], d["plan"]["split_rows"]),
+                               "rows)" % (d["plan"]["load_mode"], d["plan"]["waves"], d["plan"]["splits"],
+                                          d["plan"]["split_rows"]),
                      "bytes_per_launch": d["bytes_per_launch"], "us_per_launch": round(d["us_per_launch"], 3),
                      "alu": alu_line(d["us_per_launch"])},
         "device_curve": d["curve"],

@@ -1115,6 +1115,35 @@ hipError_t launch_spin(hipStream_t stream, uint32_t us) {
 }
 }  // namespace kvd
 
+namespace kvd {
+namespace {
+
+// Every K/V base and row stride of the call is a multiple of 16 bytes (the
+// 16-byte load modes need it).
+bool wide_segments(const kvd_attn_args* a) {
+    for (size_t i = 0; i < (size_t)a->n_seq * a->n_seg; ++i) {
+        const kvd_kv_seg& g = a->segs[i];
+        const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
+        if (g.n_rows > 0 && (((uintptr_t)g.k | (uintptr_t)g.v) % 16 || g.row_stride % 16 || vs % 16)) return false;
+    }
+    return true;
+}
+
+// The decode kernel's load mode (its WIDE argument) for a launch of n_items
+// workgroups.  16-byte loads go straight into LDS where a CU runs at most 8
+// waves (8-wave workgroups, or 4-wave ones at most two per CU): 4096 rows
+// 8.45 -> 8.25 us per call, 16384 rows 14.1 -> 13.5, 32768 rows 21.3 ->
+// 20.2.  With 12 waves per CU, register staging is faster (131072 rows 58.5
+// against 59.9 us; the 16-sequence batch's three 4-wave workgroups per CU
+// 48.7 against 50.6).
+int load_mode(bool wide, int waves, int64_t n_items, int n_cus) {
+    if (!wide) return 0;
+    return (waves == 8 || (waves == 4 && n_items <= 2 * (int64_t)n_cus)) ? 2 : 1;
+}
+
+}  // namespace
+}  // namespace kvd
+
 extern "C" int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes) {
     clear_error();
     if (!bytes) return fail(KVD_EINVAL, "bytes is NULL");
@@ -1137,6 +1166,19 @@ extern "C" int kvd_attend_plan(const kvd_attn_args* args, int32_t* split_rows, i
     return KVD_OK;
 }
 
+extern "C" int kvd_attend_load_mode(const kvd_attn_args* args, int32_t* mode) {
+    clear_error();
+    if (!mode) return fail(KVD_EINVAL, "mode is NULL");
+    AttendPlan p;
+    const int rc = plan_attend(args, &p, device_cus());
+    if (rc != KVD_OK) return rc;
+    const int ns = args->n_seq < kMaxSeqPerLaunch ? args->n_seq : kMaxSeqPerLaunch;  // the first launch
+    int64_t nsplit = 0;
+    for (int j = 0; j < ns; ++j) nsplit += p.seq[j].n_split;
+    *mode = load_mode(wide_segments(args), p.waves, nsplit * args->n_head_kv, p.n_cus);
+    return KVD_OK;
+}
+
 namespace kvd {
 namespace {
 
@@ -1155,12 +1197,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
                         a->workspace ? a->workspace_bytes : (size_t)0);
         if ((uintptr_t)a->workspace % 256) return fail(KVD_EINVAL, "workspace must be 256-byte aligned");
     }
-    bool wide = true;
-    for (size_t i = 0; i < (size_t)a->n_seq * a->n_seg; ++i) {
-        const kvd_kv_seg& g = a->segs[i];
-        const int64_t vs = g.v_row_stride ? g.v_row_stride : g.row_stride;
-        if (g.n_rows > 0 && (((uintptr_t)g.k | (uintptr_t)g.v) % 16 || g.row_stride % 16 || vs % 16)) wide = false;
-    }
+    const bool wide = wide_segments(a);
     const combine_fn ck = pick_combine(a->head_dim);
 
     uint8_t* ws = (uint8_t*)a->workspace;
@@ -1229,15 +1266,7 @@ int launch_attend(const kvd_attn_args* a, void* stream, float* part) {
         L.n_items = (int32_t)(nsplit * a->n_head_kv);
         L.split_off = (int32_t)base0;
         L.scale_log2e = scale_log2e;
-        // 16-byte loads go straight into LDS where a CU runs at most 8 waves
-        // (8-wave workgroups, or 4-wave ones at most two per CU): 4096 rows
-        // 8.45 -> 8.25 us per call, 16384 rows 14.1 -> 13.5, 32768 rows
-        // 21.3 -> 20.2.  With 12 waves per CU, register staging is faster
-        // (131072 rows 58.5 against 59.9 us; the 16-sequence batch's three
-        // 4-wave workgroups per CU 48.7 against 50.6).
-        const int mode = !wide ? 0
-                         : (p.waves == 8 || (p.waves == 4 && L.n_items <= 2 * (int64_t)p.n_cus)) ? 2
-                                                                                                 : 1;
+        const int mode = load_mode(wide, p.waves, L.n_items, p.n_cus);
         const decode_fn dk = pick_decode(a->head_dim, p.group, a->v_type, mode, p.waves);
         if (!dk) return fail(KVD_EINVAL, "no kernel for head_dim %d, group %d", a->head_dim, p.group);
         const unsigned grid = (unsigned)((L.n_items + 7) / 8 * 8);  // the kernel assumes this rounding

@@ -93,6 +93,8 @@ def _declare(L):
     L.kvd_attend_plan.restype = c_int
     L.kvd_attend_plan.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_int32),
                                   ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+    L.kvd_attend_load_mode.restype = c_int
+    L.kvd_attend_load_mode.argtypes = [ctypes.POINTER(AttnArgs), ctypes.POINTER(ctypes.c_int32)]
     L.kvd_attend_decode.restype = c_int
     L.kvd_attend_decode.argtypes = [ctypes.POINTER(AttnArgs), c_void_p]
     L.kvd_attend_decode_noalloc.restype = c_int
@@ -236,6 +238,14 @@ def attend_plan(args: AttnArgs):
     sr, w, ns = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int64(0)
     _check(lib().kvd_attend_plan(ctypes.byref(args), ctypes.byref(sr), ctypes.byref(w), ctypes.byref(ns)))
     return int(sr.value), int(w.value), int(ns.value)
+
+
+def attend_load_mode(args: AttnArgs) -> int:
+    """The decode kernel's load mode for the call's first launch (0 dword, 1
+    16-byte via registers, 2 16-byte straight into LDS)."""
+    m = ctypes.c_int32(-1)
+    _check(lib().kvd_attend_load_mode(ctypes.byref(args), ctypes.byref(m)))
+    return int(m.value)
 
 
 class Workspace:

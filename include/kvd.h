@@ -186,6 +186,17 @@ int kvd_attend_workspace_bytes(const kvd_attn_args* args, size_t* bytes);
  * split-K decode over row ranges, merged by running maxima and sums). */
 int kvd_attend_plan(const kvd_attn_args* args, int32_t* split_rows, int32_t* waves, int64_t* total_splits);
 
+/* How the decode kernel of the call's first launch loads K/V ("F5 -- Advanced
+ * KV Cache Techniques", M4: the split-K decode kernel this describes): 0 =
+ * dword loads (some K/V base or row stride is not a multiple of 16 bytes),
+ * 1 = 16-byte loads staged in registers, 2 = 16-byte loads straight into LDS
+ * (where a compute unit runs at most 8 waves: 8-wave workgroups, or 4-wave
+ * ones at most two per compute unit).  Validates the arguments like
+ * kvd_attend_plan and launches nothing.  Returns KVD_OK and sets *mode, or
+ * KVD_EINVAL (also for a NULL mode).  For profiling: the mode is the
+ * kernel's fourth template argument in a trace. */
+int kvd_attend_load_mode(const kvd_attn_args* args, int32_t* mode);
+
 /* Enqueue decode attention on `stream` (asynchronous).  Returns KVD_OK,
  * KVD_EINVAL (bad shapes, unaligned or null pointers, a sequence with no
  * visible row, workspace too small) or KVD_EHIP (launch failure). */

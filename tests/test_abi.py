@@ -193,6 +193,25 @@ def test_plan_fill_rule(seg_lists, plan):
     assert _plan_of(seg_lists) == plan
 
 
+@pytest.mark.parametrize("seg_lists,stride,mode", [
+    ([[(4096, 0)]], 1088, 2),            # 4 waves, one workgroup per CU: straight into LDS
+    ([[(16384, 0)]], 1088, 2),           # 8 waves
+    ([[(131072, 0)]], 1088, 1),          # 12 waves: staged in registers
+    ([[(n, 0)] for n in (256, 322, 406, 512, 645, 812, 1024, 1290, 1625, 2048, 2580, 3250, 4096, 5160, 6501, 8192)],
+     1088, 1),                           # 4 waves, about three per CU
+    ([[(4096, 0)]], 1096, 0),            # a row stride that is not a multiple of 16: dword loads
+])
+def test_load_mode(seg_lists, stride, mode):
+    """kvd_attend_load_mode: the decode kernel's load mode for the call's first
+    launch, from the plan and the alignment of the K/V pointers and strides
+    (256 CUs)."""
+    segs = [kvd.KvSeg(0x10000, 0x20000, n, p0, stride) for sl in seg_lists for n, p0 in sl]
+    a, _ = _args(n_seq=len(seg_lists), n_seg=len(seg_lists[0]))
+    a.segs = (kvd.KvSeg * len(segs))(*segs)
+    assert kvd.attend_load_mode(a) == mode
+    assert kvd.lib().kvd_attend_load_mode(ctypes.byref(a), None) == kvd.KVD_EINVAL
+
+
 @pytest.mark.parametrize("n_seq,n,plan", [(16, 4096, (2048, 12, 32)), (17, 4096, (384, 4, 187)),
                                           (32, 4096, (2048, 12, 64)), (64, 4096, (2048, 12, 128)),
                                           (64, 1024, (512, 8, 128))])
